@@ -1,0 +1,196 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache attention (PagedAttention) on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  A sequence's keys and values live in fixed-size physical
+ * blocks of B tokens drawn from one pool, and a per-sequence block table maps
+ * logical block j / B to its physical block ("Configuring vLLM and
+ * PagedAttention for High Throughput Enterprise LLM Serving", section
+ * "Architectural Foundations: PagedAttention & Virtual Memory", attention
+ * equation and the block-table lookup after it).  Attention is the plain
+ * softmax(q.k^T * scale) V over the sequence's keys in logical order; the
+ * paging only changes where keys and values are read from.  Blocks hold 16 or
+ * 32 tokens ("vLLM Guide: High-Throughput Multi-GPU LLM Serving with
+ * PagedAttention", section "What Is PagedAttention?").
+ *
+ * Layouts (row-major, contiguous, element type given by `dtype`):
+ *   key_cache, value_cache : [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_tables           : int32 [rows][max_blocks_per_seq]
+ *   decode query / out     : [num_seqs][num_q_heads][head_dim]
+ *   prefill query / out    : [total_query_tokens][num_q_heads][head_dim]
+ *   new key / value        : [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping           : int64 [num_tokens], slot = block * block_size + offset
+ * Grouped-query attention: q head h reads kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Conventions shared by every entry point.
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library allocates no memory and keeps no pointer after it returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call never synchronises.  Results are visible once the stream
+ *     reaches that point.
+ *   - Argument checks run on the host before anything is launched.  Any
+ *     status other than PA_OK means nothing was enqueued; pa_last_error()
+ *     then returns a thread-local description.
+ *   - Device-side data are not validated on the host (that would need a
+ *     synchronising copy).  Kernels stay inside the buffers whatever the
+ *     data: a block-table entry outside [0, num_blocks) makes those tokens
+ *     count as absent, a slot outside [0, num_blocks * block_size) is skipped,
+ *     and context lengths are clamped to max_blocks_per_seq * block_size.
+ *     Such inputs are caller errors and their results are unspecified.
+ *   - Supported: dtype PA_F32 or PA_BF16 (prefill: PA_BF16 only), head_dim
+ *     64 or 128, block_size 16 or 32, num_q_heads / num_kv_heads in
+ *     {1, 2, 4, 8}.  Other shapes return PA_ERR_UNSUPPORTED.
+ *   - All pointers must be 16-byte aligned (PA_ERR_INVALID_ARG otherwise).
+ *   - Entry points are reentrant; concurrent calls on different streams must
+ *     not share output or workspace buffers.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, inconsistent shape */
+    PA_ERR_UNSUPPORTED = 2,  /* dtype, head_dim, block_size or group size not built */
+    PA_ERR_WORKSPACE = 3,    /* decode workspace missing or too small */
+    PA_ERR_HIP = 4           /* the HIP runtime refused the launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int32_t pa_abi_version(void);
+
+/* Short name of a status code. */
+const char *pa_status_string(int32_t status);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char *pa_last_error(void);
+
+/*
+ * pa_reshape_and_cache -- write the keys and values of new tokens into their
+ * slots of the block pools.
+ *
+ * For every t < num_tokens with slot_mapping[t] >= 0: block = slot / block_size,
+ * offset = slot % block_size, and for each kv head h the head_dim elements
+ * key[t][h][:] are copied bit for bit to key_cache[block][h][offset][:] (and
+ * value likewise).  Negative slots are padding and are skipped.  Slots must be
+ * distinct (two tokens writing one slot race).  Blocks are taken on demand as
+ * sequences grow, which is why a new token can land anywhere in the pool
+ * ("Configuring vLLM and PagedAttention ...", section "Architectural
+ * Foundations: PagedAttention & Virtual Memory").
+ *
+ * key, value      : [num_tokens][num_kv_heads][head_dim], read
+ * key_cache, value_cache : pools, written only at the given slots
+ * num_tokens == 0 is valid and enqueues nothing.
+ */
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, int32_t dtype,
+                               void *stream);
+
+/*
+ * Partition size (tokens of one sequence handled by one workgroup) that
+ * pa_decode uses when called with partition_size == 0.  A multiple of
+ * block_size.
+ */
+int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t max_context_len, int32_t block_size);
+
+/*
+ * Bytes of device workspace pa_decode needs (0 is never returned for valid
+ * input; a small minimum is always asked).  partition_size 0 = automatic,
+ * resolved exactly as pa_decode resolves it.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode -- one query token per sequence against its paged context.
+ *
+ * out[s][h][:] = sum_j A_j V_s[j],  A_j = exp(x_j) / sum_m exp(x_m),
+ * x_j = scale * (query[s][h] . K_s[j]), j < context_lens[s],
+ * with K_s[j] = key_cache[block_tables[s][j / block_size]][h / G][j % block_size]
+ * (the attention equation and block-table lookup of "Configuring vLLM and
+ * PagedAttention ...", section "Architectural Foundations"); decode reads every
+ * cached key and value once, which is what bounds it by memory bandwidth
+ * (same page, section "Memory Bottlenecks in Autoregressive LLM Inference").
+ * context_lens[s] == 0 gives zeros.  The new token of a step is expected to
+ * be in the cache already (pa_reshape_and_cache first), so it is at position
+ * context_lens[s] - 1.
+ *
+ * Each sequence is split into partitions of partition_size tokens (0 =
+ * automatic); partitions are reduced by a second kernel through the
+ * workspace (fp32 running max, sum and unnormalised output per partition).
+ * max_context_len must be >= every context_lens[s]; it sizes the launch.
+ * Inputs are bf16 or fp32; arithmetic is fp32; out is written in dtype
+ * (bf16 by round-to-nearest-even).
+ */
+pa_status pa_decode(void *out, const void *query, const void *key_cache,
+                    const void *value_cache, const int32_t *block_tables,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                    int32_t partition_size, float scale, int32_t dtype, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * The two phases of pa_decode, callable on their own (same arguments; the
+ * pair enqueued back to back on one stream is exactly pa_decode).
+ * pa_decode_partitions writes the final output of every sequence that fits in
+ * one partition and the per-partition partial results of the others into the
+ * workspace; pa_decode_reduce merges those partials (log-sum-exp rescaling)
+ * into out and writes zeros for empty contexts.
+ */
+pa_status pa_decode_partitions(void *out, const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, int32_t max_context_len,
+                               int32_t partition_size, float scale, int32_t dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+pa_status pa_decode_reduce(void *out, const int32_t *context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                           const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_prefill_chunk -- a chunk of consecutive prompt tokens attends causally to
+ * the paged cache ("Configuring vLLM and PagedAttention ...", section
+ * "High-Throughput Batching: Continuous Batching & Chunked Prefill": long
+ * prompts are split into chunks of e.g. 512 tokens; the prefill phase is
+ * compute-bound, section "Memory Bottlenecks in Autoregressive LLM
+ * Inference").
+ *
+ * Chunk c owns query rows cu_query_lens[c] .. cu_query_lens[c+1]-1 (n_c rows)
+ * and context_lens[c] keys in the cache, which include the chunk's own
+ * tokens (written by pa_reshape_and_cache first).  Query i of the chunk is at
+ * position context_lens[c] - n_c + i and attends to keys 0 .. that position.
+ * block_tables has one row per chunk.  max_query_len >= every n_c sizes the
+ * launch.  bf16 only: QK^T and PV run on the matrix cores (bf16 inputs, fp32
+ * accumulation), softmax in fp32, out in bf16.
+ */
+pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *cu_query_lens, const int32_t *context_lens,
+                           int32_t num_chunks, int32_t max_query_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           int32_t dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,133 @@
+"""CPU oracle for paged KV-cache attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never does.
+
+Thin ctypes wrappers over ``liboracle.so`` (plain C, fp64, see pa_oracle.c).
+Inputs are CPU torch tensors exactly as produced by the workload generator;
+bf16 tensors are passed as their raw 16-bit patterns.
+
+Parity pins: every function here is pinned by tests/test_oracle.py against
+the pages' worked examples, closed forms, invariants and library routines
+(torch's scaled_dot_product_attention in fp64).  None is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_DT = {torch.float32: 0, torch.bfloat16: 1}
+STATUS = {0: "ok", 1: "invalid argument", 2: "block id out of range",
+          3: "slot out of range", 4: "duplicate slot", 5: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"oracle status {code}: {STATUS.get(code, '?')}")
+        self.code = code
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(p)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.oracle_gather.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i64, i32]
+    lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                  ctypes.c_float, i32, vp]
+    lib.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   i64, ctypes.c_float, i32]
+    lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32]
+    for f in (lib.oracle_gather, lib.oracle_decode, lib.oracle_prefill,
+              lib.oracle_reshape_and_cache):
+        f.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(t: torch.Tensor) -> int:
+    assert t.device.type == "cpu" and t.is_contiguous()
+    return t.data_ptr()
+
+
+def _check(code: int):
+    if code:
+        raise OracleError(code)
+
+
+def _i32(t) -> torch.Tensor:
+    return torch.as_tensor(t, dtype=torch.int32).contiguous()
+
+
+def gather(cache: torch.Tensor, block_table_row, length: int, kv_head: int, lib=None) -> np.ndarray:
+    """Keys (or values) of one sequence and kv head in logical order: [L, D] fp64."""
+    lib = lib or load()
+    NB, Hkv, B, D = cache.shape
+    bt = _i32(block_table_row)
+    out = np.zeros((max(length, 0), D), dtype=np.float64)
+    cache = cache.contiguous()
+    _check(lib.oracle_gather(out.ctypes.data, _ptr(cache), _ptr(bt), length, Hkv, kv_head, B,
+                             D, NB, _DT[cache.dtype]))
+    return out
+
+
+def decode(query, key_cache, value_cache, block_tables, context_lens, scale: float,
+           return_weights: bool = False, lib=None):
+    """fp64 decode attention: out [S, Hq, D] (and weights [S, Hq, MBS*B])."""
+    lib = lib or load()
+    S, Hq, D = query.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    assert D == D2 and key_cache.dtype == query.dtype == value_cache.dtype
+    bt, lens = _i32(block_tables), _i32(context_lens)
+    mbs = bt.shape[1] if bt.dim() == 2 else 0
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    w = np.zeros((S, Hq, mbs * B), dtype=np.float64) if return_weights else None
+    q, kc, vc = query.contiguous(), key_cache.contiguous(), value_cache.contiguous()
+    _check(lib.oracle_decode(out.ctypes.data, _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt),
+                             _ptr(lens), S, Hq, Hkv, D, B, mbs, NB, ctypes.c_float(scale),
+                             _DT[q.dtype], w.ctypes.data if w is not None else None))
+    return (out, w) if return_weights else out
+
+
+def prefill(query, key_cache, value_cache, block_tables, cu_query_lens, context_lens,
+            scale: float, lib=None) -> np.ndarray:
+    """fp64 causal chunk attention over the paged cache: out [Tq, Hq, D]."""
+    lib = lib or load()
+    Tq, Hq, D = query.shape
+    NB, Hkv, B, _ = key_cache.shape
+    bt, cu, lens = _i32(block_tables), _i32(cu_query_lens), _i32(context_lens)
+    C = lens.numel()
+    out = np.zeros((Tq, Hq, D), dtype=np.float64)
+    q, kc, vc = query.contiguous(), key_cache.contiguous(), value_cache.contiguous()
+    _check(lib.oracle_prefill(out.ctypes.data, _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cu),
+                              _ptr(lens), C, Hq, Hkv, D, B, bt.shape[1], NB,
+                              ctypes.c_float(scale), _DT[q.dtype]))
+    return out
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, lib=None):
+    """Bitwise scatter of new K/V into copies of the pools; returns (kc, vc)."""
+    lib = lib or load()
+    T, Hkv, D = key.shape
+    NB, Hkv2, B, D2 = key_cache.shape
+    assert Hkv == Hkv2 and D == D2
+    kc, vc = key_cache.clone().contiguous(), value_cache.clone().contiguous()
+    k, v = key.contiguous(), value.contiguous()
+    slots = torch.as_tensor(slot_mapping, dtype=torch.int64).contiguous()
+    _check(lib.oracle_reshape_and_cache(_ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(slots), T,
+                                        Hkv, D, B, NB, key.element_size()))
+    return kc, vc

@@ -1,0 +1,196 @@
+"""ctypes binding of libpa.so (declared in include/pa.h).
+
+Argument marshalling only: torch tensors become device pointers, shapes become
+ints, and work goes on the caller's current HIP stream.  Every computation
+happens in the library's kernels.  If the library is not built, or a tensor is
+not on the GPU, the call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpa.so"
+_lib = None
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_F32, PA_BF16 = 0, 1
+_DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+# Every symbol include/pa.h declares, with its ctypes signature.
+_vp, _i32, _i64, _sz, _f = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                            ctypes.c_float)
+SIGNATURES = {
+    "pa_abi_version": (_i32, []),
+    "pa_status_string": (ctypes.c_char_p, [_i32]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32,
+                                    _vp]),
+    "pa_decode_auto_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
+                         _i32, _i32, _f, _i32, _vp, _sz, _vp]),
+    "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _i64, _i32, _i32, _f, _i32, _vp, _sz, _vp]),
+    "pa_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _vp, _sz, _vp]),
+    "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _i64, _f, _i32, _vp]),
+}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("PA_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load():
+    """Load libpa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m "
+                           f"paged_kv_cache_262_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    try:
+        return load().pa_status_string(status).decode()
+    except Exception:
+        return f"status {status}"
+
+
+def _check(status: int):
+    if status != PA_OK:
+        detail = load().pa_last_error().decode()
+        if status in (PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE):
+            raise PAError(status, detail)
+        raise PAError(status, detail)
+
+
+def _dev(t: Optional[torch.Tensor], name: str) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, stream=None):
+    """Scatter new K/V [T, Hkv, D] into the pools [NB, Hkv, B, D] at slot_mapping."""
+    T, Hkv, D = key.shape
+    NB, _, B, _ = key_cache.shape
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    _check(load().pa_reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"), T, Hkv, D, B, NB,
+        _dtype(key), _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_context_len, partition_size=0) -> int:
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                block_size, max_context_len, partition_size))
+
+
+def auto_partition_size(num_seqs, num_kv_heads, max_context_len, block_size) -> int:
+    return int(load().pa_decode_auto_partition_size(num_seqs, num_kv_heads, max_context_len,
+                                                    block_size))
+
+
+def _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                 max_context_len, partition_size, scale, workspace):
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = key_cache.shape
+    mbs = block_tables.shape[1]
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    return (_dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+            _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+            _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, mbs, NB, int(max_context_len),
+            int(partition_size), float(scale), _dtype(query), _dev(workspace, "workspace"),
+            0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def make_workspace(query, key_cache, max_context_len, partition_size=0):
+    S, Hq, D = query.shape
+    _, Hkv, B, _ = key_cache.shape
+    n = decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def decode(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+           max_context_len, partition_size=0, workspace=None, stream=None):
+    """One query per sequence against the paged cache; writes ``out`` [S, Hq, D]."""
+    if workspace is None:
+        workspace = make_workspace(query, key_cache, max_context_len, partition_size)
+    _check(load().pa_decode(*_decode_args(out, query, key_cache, value_cache, block_tables,
+                                          context_lens, max_context_len, partition_size, scale,
+                                          workspace), _stream(stream)))
+    return out
+
+
+def decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size, workspace, stream=None):
+    _check(load().pa_decode_partitions(*_decode_args(out, query, key_cache, value_cache,
+                                                     block_tables, context_lens, max_context_len,
+                                                     partition_size, scale, workspace),
+                                       _stream(stream)))
+
+
+def decode_reduce(out, context_lens, num_kv_heads, block_size, max_blocks_per_seq,
+                  max_context_len, partition_size, workspace, stream=None):
+    S, Hq, D = out.shape
+    _check(load().pa_decode_reduce(
+        _dev(out, "out"), _dev(context_lens, "context_lens"), S, Hq, num_kv_heads, D, block_size,
+        max_blocks_per_seq, int(max_context_len), int(partition_size), _dtype(out),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def prefill_chunk(out, query, key_cache, value_cache, block_tables, cu_query_lens,
+                  context_lens, scale, max_query_len, stream=None):
+    """Causal chunks [Tq, Hq, D] against the paged cache; writes ``out``."""
+    Tq, Hq, D = query.shape
+    NB, Hkv, B, _ = key_cache.shape
+    C = context_lens.numel()
+    _check(load().pa_prefill_chunk(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+        _dev(cu_query_lens, "cu_query_lens"), _dev(context_lens, "context_lens"), C,
+        int(max_query_len), Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
+        _dtype(query), _stream(stream)))
+    return out
