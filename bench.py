@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: the cache write of the
+step's new K/V tokens (pa_reshape_and_cache), then decode attention over every
+sequence's paged context (pa_decode_partitions + pa_decode_reduce), plus the
+prefill chunks when the workload has them (pa_prefill_chunk).  The default
+workload is the Llama-3-8B-shaped decode layer: 64 sequences, 32 q / 8 kv
+heads, head_dim 128, bf16, 16-token blocks, contexts uniform in [512, 4096],
+one new token per sequence.
+
+Inputs are synthetic (seeded) and already resident in HBM when timing starts.
+Steps alternate between independent replicas of the pools so that the 256 MB
+last-level cache cannot serve a step from the previous one.
+
+Prints ONE JSON line (rank 0).  The value is the effective decode KV
+bandwidth: algorithmic KV bytes of the step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_cache_262_amd import accounting as acct  # noqa: E402
+from paged_kv_cache_262_amd import binding  # noqa: E402
+from paged_kv_cache_262_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, vendor figure
+METRIC = "paged-attn decode KV GB/s (% of HBM peak) + seq-tokens/s, 8B GQA shape"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_decode", choices=sorted(W.NAMED))
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent on the oracle baseline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+class Replica:
+    """One device copy of a workload."""
+
+    def __init__(self, case, dev):
+        self.kc = case.key_cache.to(dev)
+        self.vc = case.value_cache.to(dev)
+        self.q = case.query.to(dev)
+        self.bt = case.block_tables.to(dev)
+        self.lens = case.context_lens.to(dev)
+        self.nk = case.new_key.to(dev)
+        self.nv = case.new_value.to(dev)
+        self.slots = case.slot_mapping.to(dev)
+        self.out = torch.empty_like(self.q)
+        if case.num_chunks:
+            self.cq = case.chunk_query.to(dev)
+            self.cbt = case.chunk_block_tables.to(dev)
+            self.ccu = case.chunk_cu_query_lens.to(dev)
+            self.clens = case.chunk_context_lens.to(dev)
+            self.cout = torch.empty_like(self.cq)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Sharding is described in the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    dev = torch.device("cuda:0")
+    case = W.NAMED[args.workload]()
+    S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                        case.block_size)
+    eb = case.key_cache.element_size()
+    lens = case.context_lens.tolist()
+    maxL = case.max_context_len
+    P = args.partition_size or binding.auto_partition_size(S, Hkv, maxL, B)
+    reps = [Replica(case, dev)]
+    for _ in range(1, max(1, args.replicas)):
+        reps.append(Replica(case, dev))
+    ws = binding.make_workspace(reps[0].q, reps[0].kc, maxL, P)
+    stream = torch.cuda.current_stream()
+
+    # Algorithmic work per step.
+    unique = None
+    if case.shared_blocks is not None:
+        n_sh = case.shared_blocks.numel() * B
+        unique = n_sh + sum(L - n_sh for L in lens)
+    dec_bytes = acct.decode_bytes(lens, Hq, Hkv, D, B, eb, unique_tokens=unique)
+    kv_bytes = (sum(lens) if unique is None else unique) * acct.kv_bytes_per_token(1, Hkv, D, eb)
+    T = case.slot_mapping.numel()
+    cw_bytes = acct.cache_write_bytes(T, Hkv, D, eb)
+    chunks = []
+    if case.num_chunks:
+        cu = case.chunk_cu_query_lens.tolist()
+        chunks = [(cu[i + 1] - cu[i], int(case.chunk_context_lens[i]))
+                  for i in range(case.num_chunks)]
+    pf_flops = acct.prefill_flops(chunks, Hq, D) if chunks else 0
+    maxq = max((n for n, _ in chunks), default=0)
+
+    ev = {k: [] for k in ("cw0", "cw1", "dp0", "dp1", "dr1", "pf0", "pf1")}
+
+    def step(i, record):
+        r = reps[i % len(reps)]
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw0"].append(e)
+        if T:
+            binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw1"].append(e)
+            ev["dp0"].append(e)
+        binding.decode_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL, P, ws,
+                                  stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dp1"].append(e)
+        binding.decode_reduce(r.out, r.lens, Hkv, B, case.max_blocks_per_seq, maxL, P, ws,
+                              stream=stream)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dr1"].append(e)
+        if chunks:
+            if record:
+                ev["pf0"].append(ev["dr1"][-1])
+            binding.prefill_chunk(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens, case.scale,
+                                  maxq, stream=stream)
+            if record:
+                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["pf1"].append(e)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written",
+              file=sys.stderr, flush=True)
+        del a, b
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    print(f"warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True); e_start.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+    e_end = torch.cuda.Event(enable_timing=True); e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e_start.elapsed_time(e_end) / args.steps
+    print(f"timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
+          flush=True)
+
+    def avg_ms(a, b):
+        xs = [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
+        return sum(xs) / len(xs) if xs else 0.0
+
+    t_cw = avg_ms("cw0", "cw1")
+    t_dp = avg_ms("dp0", "dp1")
+    t_dr = avg_ms("dp1", "dr1")
+    t_pf = avg_ms("pf0", "pf1") if chunks else 0.0
+
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    dp_gbs = dec_bytes / (t_dp * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
+            "partition_size": P, "replicas": len(reps),
+            "prefill_chunks": chunks,
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "seq_tokens_per_s": round(sum(lens) / (ms_step * 1e-3), 1),
+        "new_tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "kernels_ms": {"reshape_and_cache": round(t_cw, 5), "decode_partition": round(t_dp, 5),
+                       "decode_reduce": round(t_dr, 5), "prefill_chunk": round(t_pf, 5)},
+        "roofline": {
+            "kernel": "decode_partition_kernel",
+            "bound": "hbm",
+            "achieved": round(dp_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dp_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": dec_bytes,
+        },
+    }
+    if chunks:
+        tf = pf_flops / (t_pf * 1e-3) / 1e12
+        result["prefill_roofline"] = {"kernel": "prefill_chunk_kernel", "bound": "mfma",
+                                      "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                      "unit": "TFLOP/s",
+                                      "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "algorithmic_flops_per_launch": pf_flops}
+    if T:
+        result["cache_write"] = {"ms": round(t_cw, 5), "bytes": cw_bytes,
+                                 "GB/s": round(cw_bytes / (t_cw * 1e-3) / 1e9, 1)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, kv_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, min_seconds, kv_bytes):
+    """The fp64 oracle (test infrastructure, as it stands) on the same decode
+    workload, on this host's cores, repeated until min_seconds have passed."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    kc, vc = (oracle.reshape_and_cache(case.new_key, case.new_value, case.key_cache,
+                                       case.value_cache, case.slot_mapping)
+              if case.slot_mapping.numel() else (case.key_cache, case.value_cache))
+    runs, t = 0, 0.0
+    while t < min_seconds or runs == 0:
+        t0 = time.perf_counter()
+        oracle.decode(case.query, kc, vc, case.block_tables, case.context_lens, case.scale)
+        t += time.perf_counter() - t0
+        runs += 1
+    per = t / runs
+    return {"value": round(kv_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full {case.name} decode (all {case.num_seqs} seqs x "
+                      f"{case.num_q_heads} q heads, fp64), {runs} runs, "
+                      f"{per * 1e3:.1f} ms per run"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,315 @@
+// C ABI of libpa.so (include/pa.h): host-side argument checks, launch
+// geometry and error reporting.  No allocation, no synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+pa_status fail(pa_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof g_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+pa_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return PA_OK;
+    if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "%s: shape not built", what);
+    return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr size_t kMinWorkspace = 256;
+constexpr int kMinPartition = 64;
+constexpr int kMaxPartition = 1 << 20;
+
+#define CHECK_PTR(p, a)                                                             \
+    do {                                                                            \
+        if (!(p)) return fail(PA_ERR_INVALID_ARG, "%s is NULL", #p);                \
+        if (!aligned((p), (a)))                                                     \
+            return fail(PA_ERR_INVALID_ARG, "%s is not %d-byte aligned", #p, (int)(a)); \
+    } while (0)
+
+pa_status check_common(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t dtype) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0)
+        return fail(PA_ERR_INVALID_ARG, "head counts must be positive (%d, %d)", num_q_heads,
+                    num_kv_heads);
+    if (num_q_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    if (num_kv_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_kv_heads too large");
+    if (dtype != PA_F32 && dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if (!pa::decode_shape_supported(dtype, head_dim, block_size, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d, block_size %d, group %d not supported",
+                    head_dim, block_size, num_q_heads / num_kv_heads);
+    return PA_OK;
+}
+
+int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
+                          int32_t max_context_len, int32_t block_size) {
+    if (partition_size > 0) return partition_size;
+    return pa_decode_auto_partition_size(num_seqs, num_kv_heads, max_context_len, block_size);
+}
+
+struct DecodeSetup {
+    pa::DecodeArgs a;
+    size_t need;
+};
+
+pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void *key_cache,
+                       const void *value_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                       int32_t partition_size, float scale, int32_t dtype, void *workspace,
+                       size_t workspace_bytes, bool needs_inputs) {
+    pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+    if (s != PA_OK) return s;
+    if (num_seqs < 0 || num_seqs > 65535)
+        return fail(PA_ERR_INVALID_ARG, "num_seqs %d out of range [0, 65535]", num_seqs);
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
+    if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
+                    (long long)max_blocks_per_seq * block_size);
+    if (partition_size < 0 || (partition_size > 0 && (partition_size % block_size ||
+                                                       partition_size % 16 ||
+                                                       partition_size > kMaxPartition)))
+        return fail(PA_ERR_INVALID_ARG,
+                    "partition_size %d must be 0 or a multiple of block_size and 16 up to %d",
+                    partition_size, kMaxPartition);
+    if (num_seqs > 0) {
+        CHECK_PTR(out, 16);
+        CHECK_PTR(context_lens, 4);
+        if (needs_inputs) {
+            CHECK_PTR(query, 16);
+            CHECK_PTR(key_cache, 16);
+            CHECK_PTR(value_cache, 16);
+            CHECK_PTR(block_tables, 4);
+            if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
+            if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+        }
+    }
+    const int32_t P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len,
+                                        block_size);
+    const int64_t np = cdiv64(max_context_len, P);
+    const size_t need =
+        pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_context_len, partition_size);
+    const size_t o_bytes = align256((size_t)num_seqs * num_q_heads * np * head_dim * 4);
+    if (np > 1 && num_seqs > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (!aligned(workspace, 256))
+            return fail(PA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                        need);
+    }
+    pa::DecodeArgs &a = st.a;
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.max_context_len = max_context_len;
+    a.partition_size = P;
+    a.num_partitions = (int)np;
+    a.scale = scale;
+    a.dtype = dtype;
+    a.ws_o = (np > 1) ? (float *)workspace : nullptr;
+    a.ws_ml = (np > 1) ? (float *)((char *)workspace + o_bytes) : nullptr;
+    st.need = need;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return 1; }
+
+const char *pa_status_string(int32_t status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+    }
+    return "PA_UNKNOWN_STATUS";
+}
+
+const char *pa_last_error(void) { return g_error; }
+
+pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                               void *value_cache, const int64_t *slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, int32_t dtype,
+                               void *stream) {
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+    if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads <= 0");
+    if (dtype != PA_F32 && dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", dtype);
+    if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32))
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d / block_size %d not supported", head_dim,
+                    block_size);
+    if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
+    if (num_tokens == 0) return PA_OK;
+    CHECK_PTR(key, 16);
+    CHECK_PTR(value, 16);
+    CHECK_PTR(key_cache, 16);
+    CHECK_PTR(value_cache, 16);
+    CHECK_PTR(slot_mapping, 8);
+    return hip_status(pa::launch_reshape_and_cache(key, value, key_cache, value_cache,
+                                                   slot_mapping, num_tokens, num_kv_heads,
+                                                   head_dim, block_size, num_blocks,
+                                                   dtype == PA_BF16 ? 2 : 4,
+                                                   (hipStream_t)stream),
+                      "reshape_and_cache");
+}
+
+int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t max_context_len, int32_t block_size) {
+    // Enough (sequence, kv head, partition) workgroups to fill 256 CUs several
+    // times over, without cutting partitions below one 16-token unit per wave.
+    (void)block_size;
+    const int64_t pairs = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+    int32_t P = 1024;
+    while (P > kMinPartition && pairs * cdiv64(max_context_len > 0 ? max_context_len : 1, P) < 4096)
+        P /= 2;
+    return P;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                 int32_t partition_size) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+        return kMinWorkspace;
+    const int32_t P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len,
+                                        block_size);
+    if (P <= 0) return kMinWorkspace;
+    const int64_t np = cdiv64(max_context_len, P);
+    if (np <= 1) return kMinWorkspace;
+    const size_t rows = (size_t)num_seqs * num_q_heads * np;
+    return align256(rows * head_dim * 4) + align256(rows * 2 * 4);
+}
+
+pa_status pa_decode_partitions(void *out, const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, int32_t max_context_len,
+                               int32_t partition_size, float scale, int32_t dtype,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, query, key_cache, value_cache, block_tables,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                               partition_size, scale, dtype, workspace, workspace_bytes, true);
+    if (s != PA_OK) return s;
+    return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
+                      "decode_partitions");
+}
+
+pa_status pa_decode_reduce(void *out, const int32_t *context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                           const void *workspace, size_t workspace_bytes, void *stream) {
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, nullptr, nullptr, nullptr, nullptr, context_lens,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               max_blocks_per_seq, 1, max_context_len, partition_size, 1.0f,
+                               dtype, (void *)workspace, workspace_bytes, false);
+    if (s != PA_OK) return s;
+    return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
+}
+
+pa_status pa_decode(void *out, const void *query, const void *key_cache,
+                    const void *value_cache, const int32_t *block_tables,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                    int32_t partition_size, float scale, int32_t dtype, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, query, key_cache, value_cache, block_tables,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                               partition_size, scale, dtype, workspace, workspace_bytes, true);
+    if (s != PA_OK) return s;
+    s = hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream), "decode_partitions");
+    if (s != PA_OK) return s;
+    return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
+}
+
+pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *cu_query_lens, const int32_t *context_lens,
+                           int32_t num_chunks, int32_t max_query_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           int32_t dtype, void *stream) {
+    if (dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "prefill runs on bf16 matrix cores: dtype must be bf16");
+    pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
+    if (s != PA_OK) return s;
+    if (num_chunks < 0 || num_chunks > 65535)
+        return fail(PA_ERR_INVALID_ARG, "num_chunks %d out of range", num_chunks);
+    if (max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len < 0");
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
+    if (num_chunks == 0 || max_query_len == 0) return PA_OK;
+    if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    CHECK_PTR(out, 16);
+    CHECK_PTR(query, 16);
+    CHECK_PTR(key_cache, 16);
+    CHECK_PTR(value_cache, 16);
+    CHECK_PTR(block_tables, 4);
+    CHECK_PTR(cu_query_lens, 4);
+    CHECK_PTR(context_lens, 4);
+    if (!pa::prefill_shape_supported(head_dim, block_size, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "prefill shape not supported");
+    pa::PrefillArgs a;
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.cu_query_lens = cu_query_lens;
+    a.context_lens = context_lens;
+    a.num_chunks = num_chunks;
+    a.max_query_len = max_query_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.scale = scale;
+    return hip_status(pa::launch_prefill_chunk(a, (hipStream_t)stream), "prefill_chunk");
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Launchers of the gfx950 kernels, called by the C ABI layer after it has
+// validated every host-side argument.  Each returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+hipError_t launch_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                                    void *value_cache, const int64_t *slot_mapping,
+                                    int num_tokens, int num_kv_heads, int head_dim,
+                                    int block_size, int64_t num_blocks, int elem_bytes,
+                                    hipStream_t stream);
+
+struct DecodeArgs {
+    void *out;
+    const void *query, *key_cache, *value_cache;
+    const int32_t *block_tables, *context_lens;
+    int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
+    int64_t num_blocks;
+    int max_context_len, partition_size, num_partitions;
+    float scale;
+    int dtype;  // 0 f32, 1 bf16
+    float *ws_o;   // [S][Hq][num_partitions][D]
+    float *ws_ml;  // [S][Hq][num_partitions][2] (running max in log2 units, sum)
+};
+
+// Returns hipErrorNotSupported when no kernel is built for the shape.
+hipError_t launch_decode_partitions(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream);
+bool decode_shape_supported(int dtype, int head_dim, int block_size, int group);
+
+struct PrefillArgs {
+    void *out;
+    const void *query, *key_cache, *value_cache;
+    const int32_t *block_tables, *cu_query_lens, *context_lens;
+    int num_chunks, max_query_len, num_q_heads, num_kv_heads, head_dim, block_size,
+        max_blocks_per_seq;
+    int64_t num_blocks;
+    float scale;
+};
+
+hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream);
+bool prefill_shape_supported(int head_dim, int block_size, int group);
+
+}  // namespace pa

@@ -1,0 +1,119 @@
+"""The C ABI library without a GPU: it loads, exports every declared symbol,
+and rejects bad arguments on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_262_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
+# Fake device addresses: never dereferenced, every call below fails its host
+# checks before any launch.
+A = 0x10000
+A2 = 0x20000
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from paged_kv_cache_262_amd import build
+        build.build()
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(lib, s), s
+        assert s in binding.SIGNATURES, f"binding lacks {s}"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pa_abi_version() == 1
+    names = [lib.pa_status_string(i).decode() for i in range(5)]
+    assert names == ["PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE",
+                     "PA_ERR_HIP"]
+
+
+def test_auto_partition_and_workspace(lib):
+    P = lib.pa_decode_auto_partition_size(64, 8, 4096, 16)
+    assert P % 16 == 0 and 64 <= P <= 1024
+    np_ = -(-4096 // P)
+    need = lib.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0)
+    assert need >= 64 * 32 * np_ * (128 + 2) * 4
+    # one partition needs no real workspace
+    assert lib.pa_decode_workspace_bytes(4, 4, 4, 64, 16, 100, 128) == 256
+    assert lib.pa_decode_workspace_bytes(4, 4, 4, 64, 16, 0, 0) == 256
+
+
+def _decode(lib, **kw):
+    a = dict(out=A, query=A, kc=A, vc=A, bt=A, lens=A, S=4, Hq=8, Hkv=2, D=128, B=16, mbs=8,
+             NB=32, maxL=100, P=0, scale=0.1, dtype=1, ws=A2, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["lens"], a["S"],
+                         a["Hq"], a["Hkv"], a["D"], a["B"], a["mbs"], a["NB"], a["maxL"], a["P"],
+                         a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), INVALID),            # Hq not a multiple of Hkv
+    (dict(Hq=0), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(B=8), UNSUPPORTED),
+    (dict(Hq=32, Hkv=2), UNSUPPORTED),       # group 16 not built
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(query=0), INVALID),                # NULL
+    (dict(kc=A + 4), INVALID),               # misaligned
+    (dict(maxL=8 * 16 + 1), INVALID),        # beyond table capacity
+    (dict(P=24), INVALID),                   # not a multiple of the block size
+    (dict(scale=float("nan")), INVALID),
+    (dict(ws=0, maxL=100, P=64), WORKSPACE),
+    (dict(wsb=16, maxL=100, P=64), WORKSPACE),
+    (dict(NB=0), INVALID),
+    (dict(S=-1), INVALID),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.pa_last_error().decode()
+
+
+def test_reshape_rejects(lib):
+    f = lib.pa_reshape_and_cache
+    assert f(A, A, A, A, A, -1, 8, 128, 16, 10, 1, None) == INVALID
+    assert f(A, A, A, A, A, 4, 8, 100, 16, 10, 1, None) == UNSUPPORTED
+    assert f(0, A, A, A, A, 4, 8, 128, 16, 10, 1, None) == INVALID
+    assert f(A, A, A, A, A + 4, 4, 8, 128, 16, 10, 1, None) == INVALID  # slots misaligned
+    assert f(A, A, A, A, A, 4, 8, 128, 16, 0, 1, None) == INVALID
+    assert f(0, 0, 0, 0, 0, 0, 8, 128, 16, 10, 1, None) == OK  # nothing to do
+
+
+def test_prefill_rejects(lib):
+    f = lib.pa_prefill_chunk
+    args = [A, A, A, A, A, A, A, 2, 512, 32, 8, 128, 16, 160, 1000, 0.1]
+    assert f(*args, 0, None) == UNSUPPORTED          # fp32 prefill
+    bad = list(args); bad[9] = 7                       # 32 % 7
+    assert f(*bad, 1, None) == INVALID
+    bad = list(args); bad[1] = 0
+    assert f(*bad, 1, None) == INVALID
+    bad = list(args); bad[8] = -1                      # max_query_len
+    assert f(*bad, 1, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(2, 4, 64)
+    with pytest.raises(ValueError):
+        binding.reshape_and_cache(q, q, torch.zeros(4, 4, 16, 64), torch.zeros(4, 4, 16, 64),
+                                  torch.zeros(2, dtype=torch.int64))
