@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_decode", choices=sorted(W.NAMED))
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="0: balanced split over waves (default); >0: fixed partitions")
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -95,7 +96,7 @@ def main():
     eb = case.key_cache.element_size()
     lens = case.context_lens.tolist()
     maxL = case.max_context_len
-    P = args.partition_size or binding.auto_partition_size(S, Hkv, maxL, B)
+    P = args.partition_size  # 0: balanced split of all units over the waves
     reps = [Replica(case, dev)]
     for _ in range(1, max(1, args.replicas)):
         reps.append(Replica(case, dev))
@@ -201,7 +202,8 @@ def main():
             "workload": case.name,
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
-            "partition_size": P, "replicas": len(reps),
+            "split": "balanced" if P == 0 else f"partitions of {P} tokens",
+            "replicas": len(reps),
             "prefill_chunks": chunks,
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
@@ -210,7 +212,7 @@ def main():
         "kernels_ms": {"reshape_and_cache": round(t_cw, 5), "decode_partition": round(t_dp, 5),
                        "decode_reduce": round(t_dr, 5), "prefill_chunk": round(t_pf, 5)},
         "roofline": {
-            "kernel": "decode_partition_kernel",
+            "kernel": "decode_stream_kernel" if P == 0 else "decode_partition_kernel",
             "bound": "hbm",
             "achieved": round(dp_gbs, 1),
             "peak": HBM_PEAK_GBS,

@@ -8,36 +8,40 @@
 // Memory").  Decode must stream every cached K and V row from HBM once per
 // step and does little arithmetic per byte, so it is bound by memory
 // bandwidth (same page, section "Memory Bottlenecks in Autoregressive LLM
-// Inference"); the design below is therefore about feeding HBM, not about the
-// matrix cores.
+// Inference"); the design below is about feeding HBM, not about the matrix
+// cores.
 //
-// Work split (split-K).  A workgroup of NW waves owns one (sequence, kv head,
-// partition of P tokens).  All G = Hq / Hkv query heads of the kv head are
-// served by the same pass over K and V (grouped-query attention), so each K/V
-// byte is read once per kv head.  Inside the workgroup the partition is cut
-// into units of 16 tokens (a whole block for B = 16, half a block for B = 32)
-// handed round-robin to the waves.
+// Unit of work.  The keys of one (sequence, kv head) are cut into units of 16
+// tokens (a whole block for B = 16, half a block for B = 32).  A wave streams
+// units and serves all G = Hq / Hkv query heads of the kv head from the same
+// pass (grouped-query attention), so each K/V byte is read once.
 //
 // Lane mapping inside a unit.  A token row is D * sizeof(T) bytes = NCH
-// chunks of 16 bytes.  LPT lanes share a row, each holding CPL chunks
-// (chunk r + LPT * k for lane r of the group), so one 16-byte load per lane
-// covers TPP = 64 / LPT whole rows and every row segment an instruction
-// touches is LPT * 16 contiguous bytes (a full 128-byte line for LPT = 8).
-// The q.k partial sums are combined across the LPT lanes with DPP row
-// operations, never through LDS.
+// chunks of 16 bytes.  LPT lanes share a row, each holding CPL chunks (chunk
+// r + LPT * k for lane r of the group), so one 16-byte load per lane covers
+// TPP = 64 / LPT whole rows and every row segment a load touches is LPT * 16
+// contiguous bytes (a full 128-byte line for LPT = 8).  q.k partial sums are
+// combined across the LPT lanes with DPP row operations.
 //
 // Softmax.  Online softmax (Milakov & Gimelshein, "Online normalizer
-// calculation for softmax", 2018) in base 2 (scale * log2 e is folded into
-// one multiply).  Each wave keeps one reference maximum per head, identical
-// in all its lanes; it is raised only when a new logit exceeds it by more
-// than kRescaleThreshold (log2 units), so the rescale of the accumulators is
-// rare.  Any reference value gives the same result in exact arithmetic; the
-// bound keeps every weight <= 2^8.
+// calculation for softmax", 2018) in base 2, with scale * log2 e folded into
+// one multiply.  A wave keeps one reference maximum per head, the same in all
+// its lanes, and raises it only when a logit exceeds it by more than
+// kRescaleThreshold (log2 units), so rescaling the accumulators is rare.  Any
+// reference gives the same result in exact arithmetic; the bound keeps every
+// weight <= 2^8.
 //
-// Partials.  The waves' (max, sum, unnormalised output) are merged in LDS.  A
-// sequence with one partition is finished there; otherwise each partition's
-// partials go to the workspace and decode_reduce_kernel merges them with the
-// usual log-sum-exp rescaling.
+// Split of the work (split-K over the context).  Two kernels produce partial
+// results (running max, sum, unnormalised output) that a reduce kernel merges
+// with log-sum-exp rescaling:
+//   - decode_stream_kernel (the default): all units of all (sequence, kv head)
+//     pairs form one sequence; every wave takes an equal contiguous range of
+//     it, crossing pair boundaries as needed, and emits one partial record per
+//     pair it touches.  The load is balanced whatever the mix of context
+//     lengths, waves never synchronise, and a pair that falls inside one wave
+//     is finished by that wave.
+//   - decode_partition_kernel (an explicit partition size): one workgroup per
+//     (sequence, kv head, partition of P tokens), waves merged in LDS.
 #include <type_traits>
 
 #include "pa_common.h"
@@ -48,6 +52,15 @@ namespace pa {
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kUnitTokens = 16;
 constexpr int kDecodeWaves = 4;
+#ifndef PA_WIDE_GROUP
+#define PA_WIDE_GROUP 8
+#endif
+#ifndef PA_BUFFER_BUDGET
+#define PA_BUFFER_BUDGET 256
+#endif
+constexpr int kWideGroup = PA_WIDE_GROUP;       // groups >= this use 16 lanes per row
+constexpr int kBufferBudget = PA_BUFFER_BUDGET;  // VGPRs for q, accumulators and buffers
+constexpr float NEG_INF = -__builtin_inff();
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -92,12 +105,21 @@ struct DecodeShape {
     static constexpr int EB = sizeof(T);
     static constexpr int ROWB = D * EB;                 // bytes of a token row
     static constexpr int NCH = ROWB / 16;               // 16-byte chunks per row
-    static constexpr int LPT = (NCH == 8) ? 8 : (NCH == 32 ? 16 : (G <= 4 ? 8 : 16));
+    // 16 lanes per row halve the per-lane q and output registers for the
+    // larger groups, which buys one more unit in flight.
+    static constexpr int LPT = (NCH == 8) ? 8 : (NCH == 32 ? 16 : (G < kWideGroup ? 8 : 16));
     static constexpr int CPL = NCH / LPT;               // chunks per lane
     static constexpr int TPP = 64 / LPT;                // rows per load instruction
     static constexpr int NPASS = kUnitTokens / TPP;     // loads per unit, per tensor
     static constexpr int EPC = 16 / EB;                 // elements per chunk
     static constexpr int OPL = CPL * EPC;               // output elements per lane per head
+    static constexpr int UNIT_BYTES = kUnitTokens * ROWB;
+    // Units in flight + 1: as many register buffers as fit next to q, the
+    // accumulators and temporaries in the 256 VGPRs of 2 waves per SIMD.
+    static constexpr int BUF_REGS = NPASS * CPL * 8;
+    static constexpr int FIXED_REGS = G * CPL * 4 + G * OPL + NPASS * G + 40;
+    static constexpr int NBUF_FIT = (kBufferBudget - FIXED_REGS) / BUF_REGS;
+    static constexpr int NBUF = NBUF_FIT < 2 ? 2 : (NBUF_FIT > 4 ? 4 : NBUF_FIT);
     static_assert(NCH % LPT == 0 && kUnitTokens % TPP == 0, "shape");
 };
 
@@ -108,81 +130,70 @@ struct UnitRegs {
     uint4 v[S::NPASS][S::CPL];
 };
 
-template <typename T, int D, int B, int G, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
-    T *__restrict__ out, const T *__restrict__ query, const T *__restrict__ key_cache,
-    const T *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, int num_q_heads, int num_kv_heads,
-    int max_blocks, int max_tokens, int64_t num_blocks, int P, int np_max, float scale_log2,
-    float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+// Buffer resources of one unit in the K and V pools: base = the unit's first
+// byte, range = the unit, or an empty range when there is nothing to read
+// (then every load returns zeros without touching memory).  Loads are thus
+// issued unconditionally, which keeps the count of loads in flight identical
+// on every path and lets the compiler wait for exactly the unit it processes.
+struct UnitRes {
+    __amdgpu_buffer_rsrc_t k, v;
+};
+
+__device__ __forceinline__ UnitRes unit_res(const char *kbase, const char *vbase, int64_t off,
+                                            int range) {
+    return UnitRes{__builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range,
+                                                     0x00020000),
+                   __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range,
+                                                     0x00020000)};
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_unit(UnitRegs<T, D, G> &R, const UnitRes &res, int lane_off) {
     using S = DecodeShape<T, D, G>;
-    constexpr int LPT = S::LPT, CPL = S::CPL, TPP = S::TPP, NPASS = S::NPASS, EPC = S::EPC,
-                  OPL = S::OPL, ROWB = S::ROWB;
-    constexpr float NEG_INF = -__builtin_inff();
-
-    const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-    // max_tokens = min(max_blocks * B, np_max * P): lengths beyond what the
-    // table or the launch covers are clamped, so no access leaves the buffers.
-    int L = context_lens[s];
-    L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
-    const int np = cdiv(L, P);
-    if (p >= np) return;  // whole workgroup: this partition is empty
-    const int tok0 = p * P;
-    const int tok1 = min(L, tok0 + P);
-    const int nunits = cdiv(tok1 - tok0, kUnitTokens);
-    const int u_first = tok0 / kUnitTokens;
-
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int tg = lane / LPT, r = lane % LPT;
-
-    // Query chunks of the G heads of this kv head (raw, reused for every key).
-    uint4 qr[G][CPL];
-    const char *qbase = (const char *)query + ((int64_t)s * num_q_heads + (int64_t)g * G) * ROWB;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int pp = 0; pp < S::NPASS; ++pp)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k)
-            qr[h][k] = *(const uint4 *)(qbase + h * ROWB + (r + LPT * k) * 16);
+        for (int k = 0; k < S::CPL; ++k) {
+            const int a = lane_off + pp * S::TPP * S::ROWB + S::LPT * k * 16;
+            R.k[pp][k] =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res.k, a, 0, 0));
+            R.v[pp][k] =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res.v, a, 0, 0));
+        }
+}
 
-    float o[G][OPL];
+// Online-softmax state of one wave for one (sequence, kv head): the G query
+// heads, their running maxima (wave-uniform), and per-lane partial sums and
+// outputs over the rows this lane's token group has seen.
+template <typename T, int D, int G>
+struct WaveAcc {
+    using S = DecodeShape<T, D, G>;
+    uint4 q[G][S::CPL];
+    float o[G][S::OPL];
     float l[G], m[G];
+
+    __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        l[h] = 0.f;
-        m[h] = NEG_INF;
+        for (int h = 0; h < G; ++h) {
+            l[h] = 0.f;
+            m[h] = NEG_INF;
 #pragma unroll
-        for (int i = 0; i < OPL; ++i) o[h][i] = 0.f;
+            for (int i = 0; i < S::OPL; ++i) o[h][i] = 0.f;
+        }
     }
 
-    const int32_t *bt = block_tables + (int64_t)s * max_blocks;
-    const char *kbase = (const char *)key_cache;
-    const char *vbase = (const char *)value_cache;
-    const int64_t head_bytes = (int64_t)B * ROWB;
-    const int64_t block_bytes = head_bytes * num_kv_heads;
-    const int lane_off = tg * ROWB + r * 16;
+    // q rows of the G heads: qrow points at head 0 of the group.
+    __device__ __forceinline__ void load_q(const char *qrow, int r) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int k = 0; k < S::CPL; ++k)
+                q[h][k] = *(const uint4 *)(qrow + h * S::ROWB + (r + S::LPT * k) * 16);
+    }
 
-    // Byte offset of unit u (relative to the pool) and its count of valid rows.
-    auto locate = [&](int u, int &nvalid) -> int64_t {
-        const int tok = (u_first + u) * kUnitTokens;
-        int phys = uniform(bt[tok / B]);
-        nvalid = min(kUnitTokens, tok1 - tok);
-        if (phys < 0 || (int64_t)phys >= num_blocks) {
-            phys = 0;  // caller error: read a valid block, count no token
-            nvalid = 0;
-        }
-        return (int64_t)phys * block_bytes + (int64_t)g * head_bytes + (tok % B) * ROWB + lane_off;
-    };
-    auto load = [&](UnitRegs<T, D, G> &R, int64_t off) {
-#pragma unroll
-        for (int pp = 0; pp < NPASS; ++pp)
-#pragma unroll
-            for (int k = 0; k < CPL; ++k) {
-                const int64_t a = off + pp * TPP * ROWB + LPT * k * 16;
-                R.k[pp][k] = *(const uint4 *)(kbase + a);
-                R.v[pp][k] = *(const uint4 *)(vbase + a);
-            }
-    };
-    auto process = [&](UnitRegs<T, D, G> &R, int nvalid) {
+    __device__ __forceinline__ void process(UnitRegs<T, D, G> &R, int nvalid, float scale_log2,
+                                            int tg) {
+        constexpr int NPASS = S::NPASS, CPL = S::CPL, EPC = S::EPC, TPP = S::TPP;
         float sc[NPASS][G];
 #pragma unroll
         for (int pp = 0; pp < NPASS; ++pp)
@@ -190,8 +201,8 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
             for (int h = 0; h < G; ++h) {
                 float a = 0.f;
 #pragma unroll
-                for (int k = 0; k < CPL; ++k) a = chunk_dot<T>(qr[h][k], R.k[pp][k], a);
-                sc[pp][h] = group_sum<LPT>(a) * scale_log2;
+                for (int k = 0; k < CPL; ++k) a = chunk_dot<T>(q[h][k], R.k[pp][k], a);
+                sc[pp][h] = group_sum<S::LPT>(a) * scale_log2;
             }
         if (nvalid < kUnitTokens) {
             // Rows past the end of the context: weight exactly 0 and value
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
                 m[h] = mn;
                 l[h] *= alpha;
 #pragma unroll
-                for (int i = 0; i < OPL; ++i) o[h][i] *= alpha;
+                for (int i = 0; i < S::OPL; ++i) o[h][i] *= alpha;
             }
         }
 #pragma unroll
@@ -242,66 +253,369 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) o[h][k * EPC + e] = fmaf(pr[h], v[e], o[h][k * EPC + e]);
+                    for (int e = 0; e < EPC; ++e)
+                        o[h][k * EPC + e] = fmaf(pr[h], v[e], o[h][k * EPC + e]);
+            }
+        }
+    }
+
+    // Sum l and o over the wave's token groups; afterwards every lane holds
+    // the totals for the dims of its chunks.
+    __device__ __forceinline__ void reduce_groups() {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (S::LPT == 8) {
+                l[h] += dpp<DPP_ROR8>(l[h]);
+#pragma unroll
+                for (int i = 0; i < S::OPL; ++i) o[h][i] += dpp<DPP_ROR8>(o[h][i]);
+            }
+            l[h] += __shfl_xor(l[h], 16);
+            l[h] += __shfl_xor(l[h], 32);
+#pragma unroll
+            for (int i = 0; i < S::OPL; ++i) {
+                o[h][i] += __shfl_xor(o[h][i], 16);
+                o[h][i] += __shfl_xor(o[h][i], 32);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Balanced split: every wave streams an equal share of all units.
+// ---------------------------------------------------------------------------
+
+// Context length as the kernels use it: clamped to what the table holds.
+__device__ __forceinline__ int clamp_len(int L, int max_tokens) {
+    return L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
+}
+
+// Wave (of nw <= U) whose range [U*w/nw, U*(w+1)/nw) contains unit u < U.
+__device__ __forceinline__ int wave_of_unit(int64_t u, int64_t U, int nw) {
+    return (int)(((u + 1) * nw - 1) / U);
+}
+
+// Exclusive scan of the per-sequence unit counts into scan[0..S], by a
+// workgroup of NW waves.  scan[S] is the total per kv head.
+template <int NW>
+__device__ void scan_units(int *scan, const int32_t *__restrict__ context_lens, int S,
+                           int max_tokens) {
+    __shared__ int wave_sums[NW];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int per = cdiv(S, NW * 64);
+    const int lo = min(S, t * per), hi = min(S, lo + per);
+    int sum = 0;
+    for (int s = lo; s < hi; ++s) sum += cdiv(clamp_len(context_lens[s], max_tokens), kUnitTokens);
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wave_sums[w] = incl;
+    __syncthreads();
+    int run = incl - sum, total = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+        run += (ww < w) ? wave_sums[ww] : 0;
+        total += wave_sums[ww];
+    }
+    for (int s = lo; s < hi; ++s) {
+        scan[s] = run;
+        run += cdiv(clamp_len(context_lens[s], max_tokens), kUnitTokens);
+    }
+    if (t == 0) scan[S] = total;
+    __syncthreads();
+}
+
+// Largest s with scan[s] * Hkv <= u (u inside the flattened range).
+__device__ __forceinline__ int seq_of_unit(const int *scan, int S, int64_t u, int Hkv) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)scan[mid] * Hkv <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <typename T, int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
+    T *__restrict__ out, const T *__restrict__ query, const T *__restrict__ key_cache,
+    const T *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int S, int num_q_heads, int num_kv_heads,
+    int max_blocks, int max_tokens, int64_t num_blocks, int nw, float scale_log2,
+    float *__restrict__ rec_o, float *__restrict__ rec_ml, int *__restrict__ ws_scan) {
+    using SH = DecodeShape<T, D, G>;
+    constexpr int LPT = SH::LPT, CPL = SH::CPL, EPC = SH::EPC, ROWB = SH::ROWB;
+    __shared__ int scan[kStreamMaxSeqs + 1];
+    scan_units<NW>(scan, context_lens, S, max_tokens);
+    const int Hkv = num_kv_heads;
+    const int64_t U = (int64_t)scan[S] * Hkv;
+    if (blockIdx.x == 0)
+        for (int s = threadIdx.x; s <= S; s += NW * 64) ws_scan[s] = scan[s];
+
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    const int tg = lane / LPT, r = lane % LPT;
+    // With fewer units than waves only the first U waves work, so that every
+    // working wave owns at least one unit (the reduce relies on it).
+    const int nwe = (int)min((int64_t)nw, U);
+    const int gw = blockIdx.x * NW + w;
+    if (gw >= nwe) return;
+    const int64_t ua = U * gw / nwe, ub = U * (gw + 1) / nwe;
+
+    const int64_t head_bytes = (int64_t)B * ROWB;
+    const int64_t block_bytes = head_bytes * Hkv;
+    const char *kbase = (const char *)key_cache;
+    const char *vbase = (const char *)value_cache;
+    const int lane_off = tg * ROWB + r * 16;
+
+    WaveAcc<T, D, G> acc;
+    int cur_item = -1, cur_s = 0, cur_g = 0;
+
+    // Write the finished (sequence, kv head) pair: directly to out when this
+    // wave saw all of it, else as a partial record for the reduce kernel.
+    auto finish = [&]() __attribute__((always_inline)) {
+        acc.reduce_groups();
+        const int us = scan[cur_s + 1] - scan[cur_s];
+        const int64_t u0 = (int64_t)scan[cur_s] * Hkv + (int64_t)cur_g * us;
+        const bool whole = u0 >= ua && u0 + us <= ub;
+        if (tg != 0) return;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const int64_t qrow = (int64_t)cur_s * num_q_heads + (int64_t)cur_g * G + h;
+            if (whole) {
+                const float inv = acc.l[h] > 0.f ? 1.f / acc.l[h] : 0.f;
+#pragma unroll
+                for (int k = 0; k < CPL; ++k)
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e)
+                        Elem<T>::store(out + qrow * D + (r + LPT * k) * EPC + e,
+                                       acc.o[h][k * EPC + e] * inv);
+            } else {
+                const int64_t rid = (int64_t)(cur_item + gw) * G + h;
+#pragma unroll
+                for (int k = 0; k < CPL; ++k)
+#pragma unroll
+                    for (int e = 0; e < EPC; e += 4)
+                        *(float4 *)(rec_o + rid * D + (r + LPT * k) * EPC + e) =
+                            make_float4(acc.o[h][k * EPC + e], acc.o[h][k * EPC + e + 1],
+                                        acc.o[h][k * EPC + e + 2], acc.o[h][k * EPC + e + 3]);
+                if (r == 0) *(float2 *)(rec_ml + rid * 2) = make_float2(acc.m[h], acc.l[h]);
             }
         }
     };
 
-    // Two register buffers: the loads of the next unit are in flight while
-    // the current one is processed.
-    UnitRegs<T, D, G> ra, rb;
-    int na = 0, nb = 0;
-    int u = w;
-    if (u < nunits) load(ra, locate(u, na));
-    for (; u < nunits; u += 2 * NW) {
-        if (u + NW < nunits) load(rb, locate(u + NW, nb));
-        if (na > 0) process(ra, na);
-        if (u + NW >= nunits) break;
-        if (u + 2 * NW < nunits) load(ra, locate(u + 2 * NW, na));
-        if (nb > 0) process(rb, nb);
+    for (int64_t base = ua; base < ub; base += 64) {
+        const int n = (int)min((int64_t)64, ub - base);
+        // Lane k describes unit base + k: its pair, row count and block.
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0;
+        {
+            const int64_t u = base + lane;
+            if (lane < n) {
+                const int s = seq_of_unit(scan, S, u, Hkv);
+                const int us = scan[s + 1] - scan[s];
+                const int rem = (int)(u - (int64_t)scan[s] * Hkv);
+                const int g = rem / us, j = rem - g * us;
+                const int L = clamp_len(context_lens[s], max_tokens);
+                const int tok = j * kUnitTokens;
+                l_item = s * Hkv + g;
+                l_nvalid = min(kUnitTokens, L - tok);
+                l_tokoff = tok % B;
+                const int phys = block_tables[(int64_t)s * max_blocks + tok / B];
+                if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
+                l_phys = phys;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
+
+        // Unit i of the chunk, or an empty range past the current segment.
+        auto locate = [&](int i, int seg_end, int &nvalid) __attribute__((always_inline)) -> UnitRes {
+            const int ii = i & 63;
+            nvalid = (i < seg_end) ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
+            const int item = __builtin_amdgcn_readlane(l_item, ii);
+            const int phys = __builtin_amdgcn_readlane(l_phys, ii);
+            const int tokoff = __builtin_amdgcn_readlane(l_tokoff, ii);
+            const int g = item % Hkv;
+            const int64_t off = nvalid > 0 ? (int64_t)phys * block_bytes + (int64_t)g * head_bytes +
+                                                 (int64_t)tokoff * ROWB
+                                           : 0;
+            return unit_res(kbase, vbase, off, nvalid > 0 ? SH::UNIT_BYTES : 0);
+        };
+
+        // Segments: runs of units of one (sequence, kv head) pair.  At a pair
+        // boundary the previous pair is finished and the next q is loaded
+        // together with the segment's first NBUF units; inside a segment
+        // NBUF - 1 units stay in flight.
+        constexpr int NB = SH::NBUF;
+        UnitRegs<T, D, G> buf[NB];
+        int nv[NB];
+        for (int i0 = 0; i0 < n;) {
+            const int item = __builtin_amdgcn_readlane(l_item, i0);
+            const uint64_t other =
+                __builtin_amdgcn_ballot_w64(lane < n && lane > i0 && l_item != item);
+            const int i1 = other ? (int)__builtin_ctzll(other) : n;  // segment end
+            if (item != cur_item) {
+                if (cur_item >= 0) finish();
+                cur_item = item;
+                cur_s = item / Hkv;
+                cur_g = item - cur_s * Hkv;
+                acc.reset();
+                acc.load_q((const char *)query +
+                               ((int64_t)cur_s * num_q_heads + (int64_t)cur_g * G) * ROWB, r);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) load_unit(buf[b], locate(i0 + b, i1, nv[b]), lane_off);
+            for (int i = i0; i < i1; i += NB) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (nv[b] > 0) acc.process(buf[b], nv[b], scale_log2, tg);
+                    load_unit(buf[b], locate(i + NB + b, i1, nv[b]), lane_off);
+                }
+            }
+            i0 = i1;
+        }
+    }
+    if (cur_item >= 0) finish();
+}
+
+// Merge the partial records of each (sequence, q head): records of pair i
+// come from waves wave_of_unit(first unit) .. wave_of_unit(last unit), stored
+// at record i + wave.  One wave per output row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
+    T *__restrict__ out, const int *__restrict__ ws_scan, int S, int num_q_heads,
+    int num_kv_heads, int nw, const float *__restrict__ rec_o, const float *__restrict__ rec_ml) {
+    constexpr int DPL = D / 64;  // dims per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)S * num_q_heads) return;
+    const int s = (int)(row / num_q_heads), h = (int)(row - (int64_t)s * num_q_heads);
+    const int G = num_q_heads / num_kv_heads;
+    const int g = h / G, hh = h - g * G;
+    const int us = ws_scan[s + 1] - ws_scan[s];
+    if (us == 0) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, 0.f);
+        return;
+    }
+    const int64_t U = (int64_t)ws_scan[S] * num_kv_heads;
+    const int nwe = (int)min((int64_t)nw, U);  // the waves that worked (us > 0, so U > 0)
+    const int64_t u0 = (int64_t)ws_scan[s] * num_kv_heads + (int64_t)g * us;
+    const int w0 = wave_of_unit(u0, U, nwe), w1 = wave_of_unit(u0 + us - 1, U, nwe);
+    if (w0 == w1) return;  // finished by its wave
+    const int64_t item = (int64_t)s * num_kv_heads + g;
+    const int nrec = w1 - w0 + 1;
+    float M = NEG_INF;
+    for (int k = lane; k < nrec; k += 64) M = fmaxf(M, rec_ml[((item + w0 + k) * G + hh) * 2]);
+    M = wave_max(M);
+    float lsum = 0.f, acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+    for (int k = 0; k < nrec; ++k) {
+        const int64_t rid = (item + w0 + k) * G + hh;
+        const float2 ml = *(const float2 *)(rec_ml + rid * 2);
+        const float f = (ml.x == NEG_INF) ? 0.f : fast_exp2(ml.x - M);
+        lsum = fmaf(f, ml.y, lsum);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(f, rec_o[rid * D + lane * DPL + e], acc[e]);
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, acc[e] * inv);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed partitions: one workgroup per (sequence, kv head, partition).
+// ---------------------------------------------------------------------------
+
+template <typename T, int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
+    T *__restrict__ out, const T *__restrict__ query, const T *__restrict__ key_cache,
+    const T *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int num_q_heads, int num_kv_heads,
+    int max_blocks, int max_tokens, int64_t num_blocks, int P, int np_max, float scale_log2,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml) {
+    using SH = DecodeShape<T, D, G>;
+    constexpr int LPT = SH::LPT, CPL = SH::CPL, EPC = SH::EPC, ROWB = SH::ROWB;
+
+    const int p = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+    // max_tokens = min(max_blocks * B, max_context_len, np_max * P): longer
+    // lengths are clamped, so no access leaves the buffers.
+    const int L = clamp_len(context_lens[s], max_tokens);
+    const int np = cdiv(L, P);
+    if (p >= np) return;  // whole workgroup: this partition is empty
+    const int tok0 = p * P;
+    const int tok1 = min(L, tok0 + P);
+    const int nunits = cdiv(tok1 - tok0, kUnitTokens);
+    const int u_first = tok0 / kUnitTokens;
+
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    const int tg = lane / LPT, r = lane % LPT;
+
+    WaveAcc<T, D, G> acc;
+    acc.reset();
+    acc.load_q((const char *)query + ((int64_t)s * num_q_heads + (int64_t)g * G) * ROWB, r);
+
+    const int32_t *bt = block_tables + (int64_t)s * max_blocks;
+    const char *kbase = (const char *)key_cache;
+    const char *vbase = (const char *)value_cache;
+    const int64_t head_bytes = (int64_t)B * ROWB;
+    const int64_t block_bytes = head_bytes * num_kv_heads;
+    const int lane_off = tg * ROWB + r * 16;
+
+    // Units of this wave: w, w + NW, ... (at most 64, so P <= 64 * NW * 16);
+    // lane i holds the physical block of the i-th.
+    const int nmine = nunits > w ? cdiv(nunits - w, NW) : 0;
+    int lane_phys = 0;
+    {
+        const int u = w + NW * lane;
+        if (u < nunits) lane_phys = bt[((u_first + u) * kUnitTokens) / B];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // that load: vmcnt(0), once, on every path
+
+    auto locate = [&](int i, int &nvalid) __attribute__((always_inline)) -> UnitRes {
+        const int u = w + NW * i;
+        const int tok = (u_first + u) * kUnitTokens;
+        const int phys = __builtin_amdgcn_readlane(lane_phys, i & 63);
+        nvalid = (i < nmine) ? min(kUnitTokens, tok1 - tok) : 0;
+        if (phys < 0 || (int64_t)phys >= num_blocks) nvalid = 0;  // caller error
+        const int64_t off = nvalid > 0
+            ? (int64_t)phys * block_bytes + (int64_t)g * head_bytes + (tok % B) * ROWB : 0;
+        return unit_res(kbase, vbase, off, nvalid > 0 ? SH::UNIT_BYTES : 0);
+    };
+
+    constexpr int NB = SH::NBUF;
+    UnitRegs<T, D, G> buf[NB];
+    int nv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) load_unit(buf[b], locate(b, nv[b]), lane_off);
+    for (int i = 0; i < nmine; i += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (nv[b] > 0) acc.process(buf[b], nv[b], scale_log2, tg);
+            load_unit(buf[b], locate(i + NB + b, nv[b]), lane_off);
+        }
     }
 
-    // ---- merge the waves (and the token groups inside each wave) ----------
-    // Rows of 16 lanes that still hold separate token groups; with a large
-    // G * D two of them are folded first so the LDS buffer stays <= 32 KB.
-    constexpr int RS = (G * D > 512) ? 2 : 4;
-    __shared__ float red_o[NW][RS][G * D];
-    __shared__ float red_l[NW][RS][G];
+    // ---- merge the waves -------------------------------------------------------
+    acc.reduce_groups();
+    __shared__ float red_o[NW][G * D];
+    __shared__ float red_l[NW][G];
     __shared__ float red_m[NW][G];
-    if (LPT == 8) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            l[h] += dpp<DPP_ROR8>(l[h]);
-#pragma unroll
-            for (int i = 0; i < OPL; ++i) o[h][i] += dpp<DPP_ROR8>(o[h][i]);
-        }
-    }
-    if (RS == 2) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            l[h] += __shfl_xor(l[h], 16);
-#pragma unroll
-            for (int i = 0; i < OPL; ++i) o[h][i] += __shfl_xor(o[h][i], 16);
-        }
-    }
-    const int slot = (RS == 2) ? (lane >> 5) : (lane >> 4);
-    const bool row_writer = (RS == 4) || ((lane & 16) == 0);
-    if (row_writer && (LPT == 16 || (lane & 8) == 0)) {
+    if (tg == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
 #pragma unroll
                 for (int e = 0; e < EPC; ++e)
-                    red_o[w][slot][h * D + (r + LPT * k) * EPC + e] = o[h][k * EPC + e];
-    }
-    if (row_writer && (lane & 15) == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) red_l[w][slot][h] = l[h];
+                    red_o[w][h * D + (r + LPT * k) * EPC + e] = acc.o[h][k * EPC + e];
     }
     if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) red_m[w][h] = m[h];
+        for (int h = 0; h < G; ++h) {
+            red_l[w][h] = acc.l[h];
+            red_m[w][h] = acc.m[h];
+        }
     }
     __syncthreads();
 
@@ -310,86 +624,99 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
         float M = NEG_INF;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red_m[ww][h]);
-        float acc = 0.f, lsum = 0.f;
+        float o = 0.f, lsum = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
             const float mw = red_m[ww][h];
             const float f = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
-            float so = 0.f, sl = 0.f;
-#pragma unroll
-            for (int rr = 0; rr < RS; ++rr) {
-                so += red_o[ww][rr][idx];
-                sl += red_l[ww][rr][h];
-            }
-            acc = fmaf(f, so, acc);
-            lsum = fmaf(f, sl, lsum);
+            o = fmaf(f, red_o[ww][idx], o);
+            lsum = fmaf(f, red_l[ww][h], lsum);
         }
         const int64_t qrow = (int64_t)s * num_q_heads + (int64_t)g * G + h;
         if (np == 1) {
-            Elem<T>::store(out + qrow * D + d, lsum > 0.f ? acc / lsum : 0.f);
+            Elem<T>::store(out + qrow * D + d, lsum > 0.f ? o / lsum : 0.f);
         } else {
-            ws_o[(qrow * np_max + p) * D + d] = acc;
-            if (d == 0) {
-                ws_ml[(qrow * np_max + p) * 2 + 0] = M;
-                ws_ml[(qrow * np_max + p) * 2 + 1] = lsum;
-            }
+            ws_o[(qrow * np_max + p) * D + d] = o;
+            if (d == 0) *(float2 *)(ws_ml + (qrow * np_max + p) * 2) = make_float2(M, lsum);
         }
     }
 }
 
 // Merge the partitions of each (sequence, q head): with M = max_p m_p,
-// out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).  One thread per output
-// element; sequences with a single partition were finished by the partition
+// out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).  One wave per output
+// row; sequences with a single partition were finished by the partition
 // kernel, empty ones get zeros.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(
-    T *__restrict__ out, const int32_t *__restrict__ context_lens, int num_q_heads,
+__global__ __launch_bounds__(256) void decode_reduce_kernel(
+    T *__restrict__ out, const int32_t *__restrict__ context_lens, int S, int num_q_heads,
     int max_tokens, int P, int np_max, const float *__restrict__ ws_o,
     const float *__restrict__ ws_ml) {
-    constexpr float NEG_INF = -__builtin_inff();
-    const int64_t qrow = blockIdx.x;
-    const int s = (int)(qrow / num_q_heads);
-    const int d = threadIdx.x;
-    int L = context_lens[s];
-    L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
-    const int np = cdiv(L, P);
+    constexpr int DPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)S * num_q_heads) return;
+    const int s = (int)(row / num_q_heads);
+    const int np = cdiv(clamp_len(context_lens[s], max_tokens), P);
     if (np == 1) return;
     if (np == 0) {
-        Elem<T>::store(out + qrow * D + d, 0.f);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, 0.f);
         return;
     }
-    const float *ml = ws_ml + qrow * np_max * 2;
+    const float *ml = ws_ml + row * np_max * 2;
     float M = NEG_INF;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    float acc = 0.f, lsum = 0.f;
+    for (int k = lane; k < np; k += 64) M = fmaxf(M, ml[2 * k]);
+    M = wave_max(M);
+    float lsum = 0.f, acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
     for (int p = 0; p < np; ++p) {
-        const float mp = ml[2 * p];
-        const float f = (mp == NEG_INF) ? 0.f : fast_exp2(mp - M);
-        lsum = fmaf(f, ml[2 * p + 1], lsum);
-        acc = fmaf(f, ws_o[(qrow * np_max + p) * D + d], acc);
+        const float2 mlp = *(const float2 *)(ml + 2 * p);
+        const float f = (mlp.x == NEG_INF) ? 0.f : fast_exp2(mlp.x - M);
+        lsum = fmaf(f, mlp.y, lsum);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+            acc[e] = fmaf(f, ws_o[(row * np_max + p) * D + lane * DPL + e], acc[e]);
     }
-    Elem<T>::store(out + qrow * D + d, lsum > 0.f ? acc / lsum : 0.f);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, acc[e] * inv);
 }
 
 // ---- dispatch ---------------------------------------------------------------
 
-// Tokens of a sequence that the launch covers: the table's capacity and the
-// partitions in the grid.  Both kernels clamp context lengths to it.
+// Tokens of a sequence the kernels will read: the table's capacity, the
+// declared maximum context and, for fixed partitions, the partitions in the
+// grid.  Longer context lengths are clamped to it.
 static int max_tokens(const DecodeArgs &a) {
-    const int64_t by_table = (int64_t)a.max_blocks_per_seq * a.block_size;
-    const int64_t by_grid = (int64_t)a.num_partitions * a.partition_size;
-    return (int)(by_table < by_grid ? by_table : by_grid);
+    int64_t m = (int64_t)a.max_blocks_per_seq * a.block_size;
+    if (a.max_context_len < m) m = a.max_context_len;
+    if (a.stream_waves == 0) {
+        const int64_t by_grid = (int64_t)a.num_partitions * a.partition_size;
+        if (by_grid < m) m = by_grid;
+    }
+    return (int)m;
 }
 
 template <typename T, int D, int B, int G>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
-    dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, B, G, kDecodeWaves>), grid,
-                       dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
-                       (const T *)a.key_cache, (const T *)a.value_cache, a.block_tables,
-                       a.context_lens, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
-                       max_tokens(a), a.num_blocks, a.partition_size, a.num_partitions,
-                       a.scale * kLog2e, a.ws_o, a.ws_ml);
+    if (a.stream_waves > 0) {
+        dim3 grid(cdiv(a.stream_waves, kDecodeWaves));
+        hipLaunchKernelGGL((decode_stream_kernel<T, D, B, G, kDecodeWaves>), grid,
+                           dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
+                           (const T *)a.key_cache, (const T *)a.value_cache, a.block_tables,
+                           a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
+                           a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                           a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan);
+    } else {
+        dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
+        hipLaunchKernelGGL((decode_partition_kernel<T, D, B, G, kDecodeWaves>), grid,
+                           dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
+                           (const T *)a.key_cache, (const T *)a.value_cache, a.block_tables,
+                           a.context_lens, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
+                           max_tokens(a), a.num_blocks, a.partition_size, a.num_partitions,
+                           a.scale * kLog2e, a.ws_o, a.ws_ml);
+    }
     return hipGetLastError();
 }
 
@@ -429,16 +756,23 @@ bool decode_shape_supported(int dtype, int head_dim, int block_size, int group) 
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs &a, hipStream_t stream) {
-    if (a.num_seqs == 0 || a.num_partitions == 0) return hipSuccess;
+    if (a.num_seqs == 0) return hipSuccess;
+    if (a.stream_waves == 0 && a.num_partitions == 0) return hipSuccess;
     return a.dtype == 1 ? by_dim<bf16_t>(a, stream) : by_dim<float>(a, stream);
 }
 
 template <typename T, int D>
 static hipError_t launch_red(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D>),
-                       dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)), dim3(D), 0, stream,
-                       (T *)a.out, a.context_lens, a.num_q_heads, max_tokens(a), a.partition_size,
-                       a.num_partitions, a.ws_o, a.ws_ml);
+    const unsigned blocks = (unsigned)cdiv((int)((int64_t)a.num_seqs * a.num_q_heads), 4);
+    if (a.stream_waves > 0) {
+        hipLaunchKernelGGL((decode_stream_reduce_kernel<T, D>), dim3(blocks), dim3(256), 0,
+                           stream, (T *)a.out, a.ws_scan, a.num_seqs, a.num_q_heads,
+                           a.num_kv_heads, a.stream_waves, a.ws_o, a.ws_ml);
+    } else {
+        hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(blocks), dim3(256), 0, stream,
+                           (T *)a.out, a.context_lens, a.num_seqs, a.num_q_heads, max_tokens(a),
+                           a.partition_size, a.num_partitions, a.ws_o, a.ws_ml);
+    }
     return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr size_t kMinWorkspace = 256;
 constexpr int kMinPartition = 64;
-constexpr int kMaxPartition = 1 << 20;
+constexpr int kMaxPartition = 4096;  // 64 units of 16 tokens per wave, 4 waves
 
 #define CHECK_PTR(p, a)                                                             \
     do {                                                                            \
@@ -63,6 +63,43 @@ int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_
                           int32_t max_context_len, int32_t block_size) {
     if (partition_size > 0) return partition_size;
     return pa_decode_auto_partition_size(num_seqs, num_kv_heads, max_context_len, block_size);
+}
+
+// Decode work split: balanced over waves (partition_size 0, batches up to
+// kStreamMaxSeqs) or fixed partitions.
+struct DecodePlan {
+    bool stream;
+    int waves;       // balanced split
+    int32_t P;       // fixed partitions
+    int64_t np;
+    size_t o_bytes, ml_bytes, scan_bytes;
+    size_t total() const { return o_bytes + ml_bytes + scan_bytes; }
+};
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                       int32_t partition_size) {
+    DecodePlan p{};
+    const int64_t S = num_seqs > 0 ? num_seqs : 0;
+    p.stream = partition_size == 0 && S <= pa::kStreamMaxSeqs;
+    if (p.stream) {
+        const int64_t units = S * num_kv_heads * cdiv64(max_context_len > 0 ? max_context_len : 0, 16);
+        p.waves = (int)(units < pa::kStreamWaves ? (units > 0 ? units : 1) : pa::kStreamWaves);
+        const int64_t G = num_q_heads / num_kv_heads;
+        const int64_t recs = (S * num_kv_heads + p.waves) * G;
+        p.o_bytes = align256((size_t)recs * head_dim * 4);
+        p.ml_bytes = align256((size_t)recs * 2 * 4);
+        p.scan_bytes = align256((size_t)(S + 1) * 4);
+        return p;
+    }
+    p.P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len, block_size);
+    p.np = cdiv64(max_context_len, p.P);
+    if (p.np > 1) {
+        const size_t rows = (size_t)S * num_q_heads * p.np;
+        p.o_bytes = align256(rows * head_dim * 4);
+        p.ml_bytes = align256(rows * 2 * 4);
+    }
+    return p;
 }
 
 struct DecodeSetup {
@@ -103,20 +140,17 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
             if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
         }
     }
-    const int32_t P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len,
-                                        block_size);
-    const int64_t np = cdiv64(max_context_len, P);
-    const size_t need =
-        pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                  max_context_len, partition_size);
-    const size_t o_bytes = align256((size_t)num_seqs * num_q_heads * np * head_dim * 4);
-    if (np > 1 && num_seqs > 0) {
+    const DecodePlan plan = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        block_size, max_context_len, partition_size);
+    const size_t need = plan.total() > kMinWorkspace ? plan.total() : kMinWorkspace;
+    const bool uses_ws = num_seqs > 0 && (plan.stream || plan.np > 1);
+    if (uses_ws) {
         if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
         if (!aligned(workspace, 256))
             return fail(PA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-        if (workspace_bytes < need)
+        if (workspace_bytes < plan.total())
             return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
-                        need);
+                        plan.total());
     }
     pa::DecodeArgs &a = st.a;
     a.out = out;
@@ -133,12 +167,15 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_blocks = num_blocks;
     a.max_context_len = max_context_len;
-    a.partition_size = P;
-    a.num_partitions = (int)np;
+    a.partition_size = plan.stream ? 0 : plan.P;
+    a.num_partitions = plan.stream ? 0 : (int)plan.np;
+    a.stream_waves = plan.stream ? plan.waves : 0;
     a.scale = scale;
     a.dtype = dtype;
-    a.ws_o = (np > 1) ? (float *)workspace : nullptr;
-    a.ws_ml = (np > 1) ? (float *)((char *)workspace + o_bytes) : nullptr;
+    char *ws = (char *)workspace;
+    a.ws_o = uses_ws ? (float *)ws : nullptr;
+    a.ws_ml = uses_ws ? (float *)(ws + plan.o_bytes) : nullptr;
+    a.ws_scan = (uses_ws && plan.stream) ? (int *)(ws + plan.o_bytes + plan.ml_bytes) : nullptr;
     st.need = need;
     return PA_OK;
 }
@@ -204,15 +241,12 @@ int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads,
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                  int32_t partition_size) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads || partition_size < 0)
         return kMinWorkspace;
-    const int32_t P = resolve_partition(partition_size, num_seqs, num_kv_heads, max_context_len,
-                                        block_size);
-    if (P <= 0) return kMinWorkspace;
-    const int64_t np = cdiv64(max_context_len, P);
-    if (np <= 1) return kMinWorkspace;
-    const size_t rows = (size_t)num_seqs * num_q_heads * np;
-    return align256(rows * head_dim * 4) + align256(rows * 2 * 4);
+    const DecodePlan p = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, partition_size);
+    return p.total() > kMinWorkspace ? p.total() : kMinWorkspace;
 }
 
 pa_status pa_decode_partitions(void *out, const void *query, const void *key_cache,

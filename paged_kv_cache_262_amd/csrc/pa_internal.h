@@ -13,6 +13,14 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *ke
                                     int block_size, int64_t num_blocks, int elem_bytes,
                                     hipStream_t stream);
 
+// Largest batch the balanced (stream) decode split handles: its workgroups
+// scan the per-sequence unit counts in LDS.  Larger batches use fixed
+// partitions.
+constexpr int kStreamMaxSeqs = 8192;
+// Waves the balanced split spreads the work over (256 CUs x 8 resident waves
+// on MI355X); a constant, so results do not depend on the device.
+constexpr int kStreamWaves = 2048;
+
 struct DecodeArgs {
     void *out;
     const void *query, *key_cache, *value_cache;
@@ -20,10 +28,16 @@ struct DecodeArgs {
     int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
     int64_t num_blocks;
     int max_context_len, partition_size, num_partitions;
+    int stream_waves;  // > 0: balanced split over this many waves; 0: fixed partitions
     float scale;
     int dtype;  // 0 f32, 1 bf16
-    float *ws_o;   // [S][Hq][num_partitions][D]
-    float *ws_ml;  // [S][Hq][num_partitions][2] (running max in log2 units, sum)
+    // Workspace.  Fixed partitions: ws_o [S][Hq][num_partitions][D] and ws_ml
+    // [S][Hq][num_partitions][2] (max in log2 units, sum).  Balanced split:
+    // records r = pair + wave, ws_o [S*Hkv + waves][G][D], ws_ml [..][G][2],
+    // ws_scan [S + 1] (units per sequence, exclusive scan).
+    float *ws_o;
+    float *ws_ml;
+    int *ws_scan;
 };
 
 // Returns hipErrorNotSupported when no kernel is built for the shape.

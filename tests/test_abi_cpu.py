@@ -50,12 +50,15 @@ def test_status_strings_and_version(lib):
 def test_auto_partition_and_workspace(lib):
     P = lib.pa_decode_auto_partition_size(64, 8, 4096, 16)
     assert P % 16 == 0 and 64 <= P <= 1024
-    np_ = -(-4096 // P)
-    need = lib.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0)
+    # fixed partitions: (max, sum, output) per (seq, q head, partition)
+    np_ = -(-4096 // 512)
+    need = lib.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 512)
     assert need >= 64 * 32 * np_ * (128 + 2) * 4
+    # balanced split: one record per (seq, kv head) plus one per wave, G heads each
+    need = lib.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0)
+    assert need >= (64 * 8 + 2048) * 4 * (128 + 2) * 4 + 65 * 4
     # one partition needs no real workspace
     assert lib.pa_decode_workspace_bytes(4, 4, 4, 64, 16, 100, 128) == 256
-    assert lib.pa_decode_workspace_bytes(4, 4, 4, 64, 16, 0, 0) == 256
 
 
 def _decode(lib, **kw):

@@ -95,31 +95,42 @@ def test_decode_partition_size_invariance():
     apply_cache_write_gpu(c, kc, vc)
     ref = oracle_decode(c, *oracle_pools(c))
     outs = []
-    for P in (64, 256, 512, 1024, 4096):
+    for P in (0, 64, 256, 512, 1024, 4096):
         say("partition invariance P", P)
         outs.append(gpu_decode(c, kc, vc, partition_size=P))
         torch.cuda.synchronize()
         check_close(outs[-1], ref, "bf16", f"P={P}")
-    # the single-partition path (no reduce) agrees with the split ones
+    # every split (balanced, fixed, a single partition) agrees with the others
     for o in outs[:-1]:
         assert (o.float() - outs[-1].float()).abs().max().item() < 1e-2
 
 
-def test_decode_phases_equal_decode():
+@pytest.mark.parametrize("P", [0, 256])
+def test_decode_phases_equal_decode(P):
     c = W.random_case(105, "bf16", 7, 16, 4, 128, 32, 100, 3000)
     kc, vc = dev(c.key_cache), dev(c.value_cache)
     q, bt, lens = dev(c.query), dev(c.block_tables), dev(c.context_lens)
     maxL = int(c.context_lens.max())
-    say("phases vs decode")
-    ws = binding.make_workspace(q, kc, maxL, 256)
+    say("phases vs decode", P)
+    ws = binding.make_workspace(q, kc, maxL, P)
     a = torch.empty_like(q)
-    binding.decode(a, q, kc, vc, bt, lens, c.scale, maxL, 256, ws)
+    binding.decode(a, q, kc, vc, bt, lens, c.scale, maxL, P, ws)
     b = torch.empty_like(q)
-    binding.decode_partitions(b, q, kc, vc, bt, lens, c.scale, maxL, 256, ws)
-    binding.decode_reduce(b, lens, c.num_kv_heads, c.block_size, c.max_blocks_per_seq, maxL, 256,
+    binding.decode_partitions(b, q, kc, vc, bt, lens, c.scale, maxL, P, ws)
+    binding.decode_reduce(b, lens, c.num_kv_heads, c.block_size, c.max_blocks_per_seq, maxL, P,
                           ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_large_batch_uses_fixed_partitions():
+    """Batches beyond the balanced split's limit (8192 sequences) fall back to
+    automatic fixed partitions; both must agree with the oracle."""
+    c = W.random_case(115, "bf16", 8200, 8, 4, 64, 16, 1, 40, write_new=False)
+    say("large batch", c.num_seqs)
+    out = gpu_decode(c, dev(c.key_cache), dev(c.value_cache))
+    torch.cuda.synchronize()
+    check_close(out, oracle_decode(c, c.key_cache, c.value_cache), "bf16", "8200 seqs")
 
 
 def test_decode_deterministic():
