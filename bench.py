@@ -163,16 +163,23 @@ def main():
     torch.cuda.synchronize()
     print(f"warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    # The timed steps carry no events between kernels; a second pass of the
+    # same steps records one event around each kernel for the breakdown.
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start = torch.cuda.Event(enable_timing=True); e_start.record(stream)
     for i in range(args.steps):
-        step(i, True)
+        step(i, False)
     e_end = torch.cuda.Event(enable_timing=True); e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e_start.elapsed_time(e_end) / args.steps
     print(f"timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    print("per-kernel pass done", file=sys.stderr, flush=True)
 
     def avg_ms(a, b):
         xs = [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]

@@ -477,6 +477,59 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     if (cur_item >= 0) finish();
 }
 
+// Merge the nrec partial records (m_k: max in log2 units, l_k: sum, o_k:
+// unnormalised output) of one output row: with M = max_k m_k,
+// dst = sum_k o_k 2^(m_k - M) / sum_k l_k 2^(m_k - M) (log-sum-exp merge of
+// split softmax results).  Record k's (m, l) pair is at ml + k * ml_stride, its
+// output at o + k * o_stride.  Lane k loads the weights of record k, and the
+// outputs of 8 records are loaded before any is used, so a row costs a few
+// memory round trips rather than one per record.
+template <typename T, int D>
+__device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *__restrict__ ml,
+                                              int64_t ml_stride, const float *__restrict__ o,
+                                              int64_t o_stride, int nrec, int lane) {
+    constexpr int DPL = D / 64;  // dims per lane
+    typedef float vecd __attribute__((ext_vector_type(DPL)));
+    float2 w0 = make_float2(NEG_INF, 0.f);
+    if (lane < nrec) w0 = *(const float2 *)(ml + lane * ml_stride);
+    float M = w0.x;
+    for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, ml[k * ml_stride]);
+    M = wave_max(M);
+    float lsum = 0.f;
+    vecd acc = {};
+    for (int c0 = 0; c0 < nrec; c0 += 64) {
+        float2 w = w0;
+        if (c0 > 0) {
+            w = make_float2(NEG_INF, 0.f);
+            if (c0 + lane < nrec) w = *(const float2 *)(ml + (c0 + lane) * ml_stride);
+        }
+        const float f = (w.x == NEG_INF) ? 0.f : fast_exp2(w.x - M);  // 0 past nrec
+        lsum = fmaf(f, w.y, lsum);
+        const int n = min(64, nrec - c0);
+        for (int j0 = 0; j0 < n; j0 += 8) {
+            vecd v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = c0 + min(j0 + j, n - 1);  // padded slots reload a valid record
+                v[j] = *(const vecd *)(o + k * o_stride + lane * DPL);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float fj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), j0 + j));
+                acc += fj * v[j];
+            }
+        }
+    }
+    lsum = group_sum<16>(lsum);
+    lsum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 16)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 32)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 48));
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) Elem<T>::store(dst + lane * DPL + e, acc[e] * inv);
+}
+
 // Merge the partial records of each (sequence, q head): records of pair i
 // come from waves wave_of_unit(first unit) .. wave_of_unit(last unit), stored
 // at record i + wave.  One wave per output row.
@@ -503,24 +556,9 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     const int w0 = wave_of_unit(u0, U, nwe), w1 = wave_of_unit(u0 + us - 1, U, nwe);
     if (w0 == w1) return;  // finished by its wave
     const int64_t item = (int64_t)s * num_kv_heads + g;
-    const int nrec = w1 - w0 + 1;
-    float M = NEG_INF;
-    for (int k = lane; k < nrec; k += 64) M = fmaxf(M, rec_ml[((item + w0 + k) * G + hh) * 2]);
-    M = wave_max(M);
-    float lsum = 0.f, acc[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    for (int k = 0; k < nrec; ++k) {
-        const int64_t rid = (item + w0 + k) * G + hh;
-        const float2 ml = *(const float2 *)(rec_ml + rid * 2);
-        const float f = (ml.x == NEG_INF) ? 0.f : fast_exp2(ml.x - M);
-        lsum = fmaf(f, ml.y, lsum);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(f, rec_o[rid * D + lane * DPL + e], acc[e]);
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, acc[e] * inv);
+    const int64_t rid0 = (item + w0) * G + hh;
+    merge_records<T, D>(out + row * D, rec_ml + rid0 * 2, 2 * G, rec_o + rid0 * D, (int64_t)G * D,
+                        w1 - w0 + 1, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -663,24 +701,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
         for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, 0.f);
         return;
     }
-    const float *ml = ws_ml + row * np_max * 2;
-    float M = NEG_INF;
-    for (int k = lane; k < np; k += 64) M = fmaxf(M, ml[2 * k]);
-    M = wave_max(M);
-    float lsum = 0.f, acc[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float2 mlp = *(const float2 *)(ml + 2 * p);
-        const float f = (mlp.x == NEG_INF) ? 0.f : fast_exp2(mlp.x - M);
-        lsum = fmaf(f, mlp.y, lsum);
-#pragma unroll
-        for (int e = 0; e < DPL; ++e)
-            acc[e] = fmaf(f, ws_o[(row * np_max + p) * D + lane * DPL + e], acc[e]);
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, acc[e] * inv);
+    merge_records<T, D>(out + row * D, ws_ml + row * np_max * 2, 2, ws_o + row * np_max * D, D, np,
+                        lane);
 }
 
 // ---- dispatch ---------------------------------------------------------------
