@@ -14,35 +14,41 @@
 // Tiling.  A workgroup of 8 waves owns one (chunk, kv head, tile of QT
 // queries); its 128 rows are the QT queries x G = Hq / Hkv heads that share
 // the kv head, so every K/V block brought into LDS serves all of them.  The
-// waves form 4 row groups of 32 rows x 2 key parities: even and odd 64-key
-// blocks sit in LDS together and each is read by the 4 waves of its parity
-// (half the LDS traffic per matrix product of 8 waves sharing one block),
-// while two waves per SIMD still overlap one another's softmax and loads.
-// The two parities' partial softmax states are merged once at the end.  Keys advance in blocks of 64 (four 16-token or two
-// 32-token pages), gathered through the block table into LDS: K as [key][dim]
-// (row padded by 16 bytes), V transposed to [dim][key] so that the PV operand
-// of a lane is a run of consecutive keys.
+// waves form 4 row groups of 32 rows x 2 key parities: the 64-key blocks of
+// the context go in pairs, the even block to 4 waves and the odd one to the
+// other 4 (half the LDS traffic per matrix product of 8 waves sharing one
+// block).  The two parities' partial softmax states are merged at the end.
 //
-// The products are computed transposed, S^T = K Q^T and O^T = V^T P^T: the
+// Staging.  Key blocks are gathered through the block table straight from
+// HBM into LDS (global_load_lds_dwordx4: each lane moves 16 bytes, no
+// registers), one pair of blocks ahead of the pair being multiplied, in two
+// LDS stages that alternate.  K and V rows keep their memory layout
+// [key][dim]; the 16-byte chunks of each row are permuted by an XOR with a
+// function of the key so that the matrix-operand reads below hit distinct
+// LDS banks.  The block-table entries of the tile sit in an LDS window.
+//
+// Products.  They are computed transposed, S^T = K Q^T and O^T = V^T P^T.
+// The K operand (16 keys x 32 dims) is one 16-byte LDS read per lane; the
 // fp32 S^T tile a lane holds (4 consecutive keys of one row) is, after
-// conversion to bf16, exactly the P^T operand the next MFMA needs (the keys of
-// the contraction are visited in a fixed permutation shared by both
-// operands), so P never goes through LDS.
+// conversion to bf16, exactly the P^T operand the next MFMA needs (the keys
+// of the contraction are visited in a fixed permutation shared by both
+// operands), so P never goes through LDS; and the V^T operand (16 dims x 8
+// keys per lane) comes from row-major V through the transposing LDS read
+// ds_read_b64_tr_b16, 4 keys of one dim per read.
 #include "pa_common.h"
 #include "pa_internal.h"
 
 namespace pa {
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_v2 __attribute__((ext_vector_type(2)));
 typedef float floatx4_v __attribute__((ext_vector_type(4)));
-typedef float floatx2_v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8
-#endif
-constexpr int kPfWaves = PA_PREFILL_WAVES;  // waves per workgroup (2 per SIMD at 8)
+constexpr int kPfWaves = 8;         // waves per workgroup (2 per SIMD)
 constexpr int kPfRows = 128;        // rows (query x head) per workgroup
 constexpr int kKeyBlock = 64;       // keys per LDS block
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
@@ -56,103 +62,66 @@ __device__ __forceinline__ floatx4_v mfma16x16x32(const A &a, const Bv &b, float
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    floatx2_v f = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v2));
+    typedef float floatx2_v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    const floatx2_v f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));  // RNE
 }
 
-// Staging of one 64-key block from the paged pools into LDS.
-//   K: each thread moves KPT 16-byte chunks; a wave covers whole 256-byte
-//      rows, so the global reads are contiguous.
-//   V: each thread moves one 16-byte chunk of two consecutive keys and
-//      transposes them in registers (v_perm), so V^T is written one word (2
-//      keys of one dim) at a time.
-// The data are fetched into registers one block pair ahead of their use.
-template <int D, int B>
-struct KVStage {
-    static constexpr int NCH = D * 2 / 16;
-    static constexpr int KPT = kKeyBlock * NCH / (kPfWaves * 64);  // 1 or 2
-    // V: keys per thread, so that the threads cover 64 keys x NCH chunks once
-    static constexpr int VK = kKeyBlock * NCH / (kPfWaves * 64);     // 1 or 2
-    static constexpr int KPAD = D + 8;
-    static constexpr int VPAD = kKeyBlock + 4;
-    static_assert(KPT == 1 || KPT == 2, "K chunks per thread");
-    static_assert(VK == 1 || VK == 2, "V keys per thread");
-    int k_lds0, k_lds1;        // LDS element offsets of this thread's K chunks
-    int k_off0, k_off1;        // element offsets inside a page
-    int k_pg0, k_pg1;          // page index inside the block
-    int v_pg, v_off, v_lds;    // V: page in block, offset in page, LDS position
-    int vkey;                  // first of this thread's two V keys in the block
-    u32x4 k0, k1, v0, v1;      // native vectors: plain loads/stores, no memcpy
+// Max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes holding
+// one row of an MFMA result), with lane swaps instead of LDS shuffles.
+__device__ __forceinline__ float row_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
-    __device__ __forceinline__ void init(int tid, int g) {
-        const int ci0 = tid, ci1 = tid + kPfWaves * 64;
-        const int kk0 = ci0 / NCH, ch0 = ci0 - kk0 * NCH;
-        const int kk1 = ci1 / NCH, ch1 = ci1 - kk1 * NCH;
-        k_lds0 = kk0 * KPAD + ch0 * 8;
-        k_lds1 = kk1 * KPAD + ch1 * 8;
-        k_pg0 = kk0 / B;
-        k_pg1 = kk1 / B;
-        k_off0 = g * B * D + (kk0 % B) * D + ch0 * 8;
-        k_off1 = g * B * D + (kk1 % B) * D + ch1 * 8;
-        // V: thread (vkg, vc) moves chunk vc of keys VK*vkg .. VK*vkg + VK-1
-        const int vkg = tid % (kKeyBlock / VK), vc = tid / (kKeyBlock / VK);
-        vkey = VK * vkg;
-        v_pg = vkey / B;
-        v_off = g * B * D + (vkey % B) * D + vc * 8;
-        v_lds = vc * 8 * VPAD + vkey;
-    }
-    // Pages past the tile's keys and entries outside the pool (a caller error)
-    // read block 0 harmlessly; keys past the end are masked and their values
-    // zeroed in stash().
-    static __device__ __forceinline__ int64_t page_base(int phys, int64_t num_blocks,
-                                                        int64_t block_elems) {
-        return (phys >= 0 && (int64_t)phys < num_blocks) ? (int64_t)phys * block_elems : 0;
-    }
-    // Block-table entries come from the tile's LDS window, which holds the
-    // entries from page win_p0 on (index clamped to the tile's last page).
-    static __device__ __forceinline__ int page(int idx, const int *bt_s, int win_p0, int nbt) {
-        return bt_s[(idx < nbt ? idx : nbt - 1) - win_p0];
-    }
-    __device__ __forceinline__ void fetch(int key0, const int *bt_s, int win_p0, int nbt,
-                                          const bf16_t *key_cache, const bf16_t *value_cache,
-                                          int64_t block_elems, int64_t num_blocks) {
-        const int pg0 = key0 / B;
-        const int64_t kb0 = page_base(page(pg0 + k_pg0, bt_s, win_p0, nbt), num_blocks, block_elems);
-        k0 = *(const u32x4 *)(key_cache + kb0 + k_off0);
-        if (KPT > 1) {
-            const int64_t kb1 =
-                page_base(page(pg0 + k_pg1, bt_s, win_p0, nbt), num_blocks, block_elems);
-            k1 = *(const u32x4 *)(key_cache + kb1 + k_off1);
-        }
-        const int64_t vb = page_base(page(pg0 + v_pg, bt_s, win_p0, nbt), num_blocks, block_elems);
-        const u32x4 *vsrc = (const u32x4 *)(value_cache + vb + v_off);
-        v0 = vsrc[0];
-        if (VK > 1) v1 = vsrc[D / 8];
-    }
-    // K rows as they are; V transposed: the 8 dims of the two keys become 8
-    // LDS words, each holding one dim of both keys (v_perm packs the halves).
-    __device__ __forceinline__ void stash(bf16_t *Ks, bf16_t *Vt, int key0, int kend) {
-        *(u32x4 *)(&Ks[k_lds0]) = k0;
-        if (KPT > 1) *(u32x4 *)(&Ks[k_lds1]) = k1;
-        if (key0 + kKeyBlock > kend) {  // last block: values past the end read as 0
-            if (key0 + vkey >= kend) v0 = u32x4{0, 0, 0, 0};
-            if (VK > 1 && key0 + vkey + 1 >= kend) v1 = u32x4{0, 0, 0, 0};
-        }
-        if (VK > 1) {
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                *(uint32_t *)(&Vt[v_lds + 2 * w2 * VPAD]) =
-                    __builtin_amdgcn_perm(v1[w2], v0[w2], 0x05040100u);
-                *(uint32_t *)(&Vt[v_lds + (2 * w2 + 1) * VPAD]) =
-                    __builtin_amdgcn_perm(v1[w2], v0[w2], 0x07060302u);
-            }
-        } else {
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-                Vt[v_lds + 2 * w2 * VPAD] = (bf16_t)(v0[w2] & 0xffffu);
-                Vt[v_lds + (2 * w2 + 1) * VPAD] = (bf16_t)(v0[w2] >> 16);
-            }
-        }
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i & 3 of the 8-byte pieces addressed by lanes
+// (i >> 2) + 4 j, j = 0..3.  Issued as inline assembly so that the compiler
+// does not tie it to the DMA in flight into the other stage; its result is
+// only read after lds_wait(), which names the registers it completes.
+__device__ __forceinline__ s16x4 lds_read_tr16(uint32_t addr) {
+    s16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ s16x4 lds_read_tr16_off(uint32_t addr) {
+    s16x4 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+__device__ __forceinline__ void lds_wait(s16x4 (&v)[2][2][2]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
+                   "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1]));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// One 64-key block of one tensor in LDS: [key][dim] rows of ROWB bytes.  The
+// 16-byte chunk c of row k is stored at chunk position c ^ swz(k).  swz keeps
+// bit 0, so the two chunks a transposing read takes stay adjacent, and it
+// differs between the rows that share a 256-byte bank window and are read
+// together.
+template <int D>
+struct KvLds {
+    static constexpr int ROWB = D * 2;                    // bytes per row
+    static constexpr int NCH = ROWB / 16;                 // chunks per row
+    static constexpr int KPS = 1024 / ROWB;               // rows per 1 KB DMA segment
+    static constexpr int SEGS = kKeyBlock * ROWB / 1024;  // segments per block
+    static constexpr int BLOCK_BYTES = kKeyBlock * ROWB;
+    static constexpr int STAGE_BYTES = 4 * BLOCK_BYTES;   // K even, K odd, V even, V odd
+    static constexpr int SEGS_PER_WAVE = 4 * SEGS / kPfWaves;
+    static_assert(4 * SEGS % kPfWaves == 0, "segments split evenly over the waves");
+    static __device__ __forceinline__ int swz(int key) {
+        return D == 128 ? (key & 7) << 1 : ((key >> 1) & 3) << 1;
     }
 };
 
@@ -163,24 +132,20 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ cu_query_lens,
     const int32_t *__restrict__ context_lens, int num_q_heads, int num_kv_heads, int max_blocks,
     int64_t num_blocks, float scale_log2, int num_tiles, int total) {
-    constexpr int QT = kPfRows / G;            // queries per tile
-    constexpr int KS = D / 32;                 // k-steps of S^T = K Q^T
-    constexpr int DT = D / 16;                 // 16-dim tiles of O^T
-    constexpr int RT = 2;                      // 16-row tiles per wave (32 rows)
-    constexpr int KPAD = KVStage<D, B>::KPAD;  // K row stride in LDS (elements, +16 bytes)
-    constexpr int VPAD = KVStage<D, B>::VPAD;  // V^T row stride: 34 dwords, so 16 rows
-                                               // read 8 bytes each hit 32 distinct banks
-    constexpr int KS_ELEMS = kKeyBlock * KPAD, VT_ELEMS = D * VPAD;
+    using LY = KvLds<D>;
+    constexpr int QT = kPfRows / G;  // queries per tile
+    constexpr int KS = D / 32;       // k-steps of S^T = K Q^T
+    constexpr int DT = D / 16;       // 16-dim tiles of O^T
+    constexpr int RT = 2;            // 16-row tiles per wave (32 rows)
+    constexpr int ROWB = LY::ROWB;
     constexpr float NEG_INF = -__builtin_inff();
     static_assert(kPfWaves == 8 && kPfRows == 4 * RT * 16, "4 row groups x 2 key parities");
 
-    // Two key blocks resident at once (even and odd); the same memory holds the
-    // partial results of the odd waves for the final merge.
-    constexpr int STAGE_BYTES = 2 * (KS_ELEMS + VT_ELEMS) * 2;
-    constexpr int MERGE_BYTES = 4 * 64 * (DT * RT * 4 + 2 * RT) * 4;
-    __shared__ __attribute__((aligned(16))) char smem[STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES
-                                                                                : MERGE_BYTES];
-    bf16_t *const lds = (bf16_t *)smem;  // [K even][K odd][V^T even][V^T odd]
+    // Two stages in two distinct LDS arrays: the compiler then knows that the
+    // operand reads of one stage do not wait for the DMA filling the other.
+    __shared__ __attribute__((aligned(1024))) char stage_a[LY::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage_b[LY::STAGE_BYTES];
+    __shared__ int bt_s[kBtCache];
 
     // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
     // L2).  Renumber them so that the tiles of one (chunk, kv head), which
@@ -203,7 +168,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     const int kend = min(L, pos0 + nq);             // keys any row of the tile may see
     const int32_t *bt = block_tables + (int64_t)c * max_blocks;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
     const int rg = w & 3, kp = w >> 2;  // row group, key parity
 
@@ -239,21 +204,76 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
         for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] = floatx4_v{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int64_t head_elems = (int64_t)B * D;
-    const int64_t block_elems = head_elems * num_kv_heads;
+    const int64_t block_elems = (int64_t)B * D * num_kv_heads;
     const int nkb = cdiv(kend, kKeyBlock);
+    const int npairs = cdiv(nkb, 2);
     const int nbt = cdiv(kend, B);  // pages the tile reads
+
+    // ---- block-table window -------------------------------------------------
+    // Entries of pages [win_p0, win_p0 + kBtCache).  It is refilled (rarely:
+    // every 32K keys at 16-token pages) before the DMA of a pair it does not
+    // cover; barriers separate the refill from the reads on both sides.
+    constexpr int kWinBlocks = kBtCache * B / kKeyBlock;
+    static_assert(kWinBlocks % 2 == 0, "windows hold whole pairs");
+    int win_kb0 = 0, win_p0 = 0;
+    auto load_window = [&](int kb0) __attribute__((always_inline)) {
+        win_kb0 = kb0;
+        win_p0 = kb0 * (kKeyBlock / B);
+        const int cnt = min(nbt - win_p0, kBtCache);
+        for (int i = tid; i < cnt; i += kPfWaves * 64) bt_s[i] = bt[win_p0 + i];
+    };
+
+    // ---- DMA of one pair of key blocks into a stage -------------------------
+    // The stage's 4 * SEGS segments of 1 KB ([K even][K odd][V even][V odd])
+    // are split over the waves; lane i of a segment moves chunk i % NCH of row
+    // i / NCH.  Keys past kend read the row of key kend - 1 instead (data
+    // whose weight is exactly 0), so no LDS row is ever left stale.
+    const int seg_row = lane / LY::NCH, seg_ch = lane % LY::NCH;
+    auto issue_pair = [&](char *stage, int pr) __attribute__((always_inline)) {
+        const int key_pair0 = pr * 2 * kKeyBlock;
+#pragma unroll
+        for (int j = 0; j < LY::SEGS_PER_WAVE; ++j) {
+            const int seg = w * LY::SEGS_PER_WAVE + j;  // uniform
+            const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1;
+            const int s = seg % LY::SEGS;
+            if (2 * pr + bp >= nkb) continue;  // block past the tile's keys
+            const int kk = s * LY::KPS + seg_row;
+            const int key = min(key_pair0 + bp * kKeyBlock + kk, kend - 1);
+            const int phys = bt_s[key / B - win_p0];
+            const int64_t base = (phys >= 0 && (int64_t)phys < num_blocks)
+                                     ? (int64_t)phys * block_elems : 0;  // caller error: block 0
+            const bf16_t *src = (tensor ? value_cache : key_cache) + base +
+                                ((int64_t)g * B + key % B) * D + (seg_ch ^ LY::swz(kk)) * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const void *)src,
+                (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024), 16, 0, 0);
+        }
+    };
+
+    // ---- LDS operand addresses (bytes inside a block) -----------------------
+    // K operand of key tile kt, k-step ks: row kt * 16 + l16, chunk ks * 4 + lg.
+    const int k_row_off = l16 * ROWB;
+    const int k_sw = LY::swz(l16);
+    // V^T operand of dim tile dt, key half h: the lanes of group lg read rows
+    // h * 32 + 4 * lg + (l16 >> 2) (and 16 rows further), dims dt * 16 +
+    // 4 * (l16 & 3) .. + 3, i.e. chunk 2 * dt + ((l16 & 3) >> 1), half l16 & 1.
+    // The chunk bits of the offset are free in v_row_off, so the swizzled
+    // chunk is or-ed in and dim tile dt is an xor of dt << 5.
+    const int v_row = 4 * lg + (l16 >> 2);
+    const uint32_t v_lane_off = v_row * ROWB + (l16 & 1) * 8 +
+                                ((LY::swz(v_row) ^ ((l16 & 3) >> 1)) << 4);
 
     // One 64-key block of this wave's parity: S^T = K Q^T, online softmax,
     // O^T += V^T P^T.
-    auto compute = [&](const bf16_t *Kb, const bf16_t *Vb, int key0) __attribute__((always_inline)) {
+    auto compute = [&](const char *Kb, const char *Vb, int key0) __attribute__((always_inline)) {
         floatx4_v s[4][RT];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             u32x4 kf[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[ks] = *(const u32x4 *)(&Kb[(kt * 16 + l16) * KPAD + ks * 32 + lg * 8]);
+                kf[ks] = *(const u32x4 *)(Kb + kt * 16 * ROWB + k_row_off +
+                                          (((ks * 4 + lg) ^ k_sw) << 4));
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 floatx4_v a = {0.f, 0.f, 0.f, 0.f};
@@ -276,14 +296,12 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
         u32x4 pf[RT][2];  // P^T operands: [rt][32-key half]
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            // Row maximum over this block (lanes l, l+16, l+32, l+48 share a row).
             float mx = NEG_INF;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
                 mx = fmaxf(mx, fmaxf(fmaxf(s[kt][rt][0], s[kt][rt][1]),
                                      fmaxf(s[kt][rt][2], s[kt][rt][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = row_max4(mx);
             // The reference maximum m_row (log2 units) is raised only when a
             // logit exceeds it by more than kPfRescale, so the rescale of the
             // accumulators is rare; weights stay below 2^kPfRescale.
@@ -314,73 +332,70 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h) acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
         }
+        // O^T += V^T P^T, two dim tiles per batch; the transposing reads of
+        // the next batch are in flight while the current one multiplies.
+        const uint32_t vbase = lds_addr(Vb) + v_lane_off;
+        s16x4 vb[2][2][2][2];  // [buffer][dim tile of the batch][key half][rows +0 / +16]
+        auto issue_v = [&](s16x4 (&dst)[2][2][2], int dt0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16_t *vrow = &Vb[(dt * 16 + l16) * VPAD + h * 32 + lg * 4];
-                const uint2 lo = *(const uint2 *)(vrow);
-                const uint2 hi = *(const uint2 *)(vrow + 16);
-                const u32x4 vf = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    acc_o[dt][rt] = mfma16x16x32(vf, pf[rt][h], acc_o[dt][rt]);
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t a = vbase ^ ((uint32_t)(dt0 + j) << 5);
+                dst[j][0][0] = lds_read_tr16(a);
+                dst[j][0][1] = lds_read_tr16_off<16 * ROWB>(a);
+                dst[j][1][0] = lds_read_tr16_off<32 * ROWB>(a);
+                dst[j][1][1] = lds_read_tr16_off<48 * ROWB>(a);
             }
+        };
+        issue_v(vb[0], 0);
+#pragma unroll
+        for (int b = 0; b < DT / 2; ++b) {
+            lds_wait(vb[b & 1]);
+            if (b + 1 < DT / 2) issue_v(vb[(b + 1) & 1], 2 * (b + 1));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const s16x8 vf =
+                        __builtin_shufflevector(vb[b & 1][j][h][0], vb[b & 1][j][h][1], 0, 1, 2, 3,
+                                                4, 5, 6, 7);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        acc_o[2 * b + j][rt] = mfma16x16x32(vf, pf[rt][h], acc_o[2 * b + j][rt]);
+                }
         }
     };
 
-    // Blocks go in pairs: stage 0 holds the even block, stage 1 the odd one.
-    // Each stage's next block is fetched while the current pair is multiplied.
-    KVStage<D, B> st0, st1;
-    st0.init(tid, g);
-    st1.init(tid, g);
-    // Page lookups read an LDS window of the block table, so that they never
-    // wait on global loads queued behind the K/V prefetch.  A window covers
-    // kWinBlocks key blocks plus the two the pipeline fetches ahead; it is
-    // refilled (rarely: every 32K keys at 16-token pages) at the top of an
-    // iteration, where the stash waits for all loads anyway.
-    constexpr int kWinBlocks = kBtCache * B / kKeyBlock - 2;
-    static_assert(kWinBlocks > 0 && kWinBlocks % 2 == 0, "window steps by block pairs");
-    __shared__ int bt_s[kBtCache];
-    int win_p0 = 0, next_win = kWinBlocks;
-    auto load_window = [&](int kb0) __attribute__((always_inline)) {
-        win_p0 = kb0 * (kKeyBlock / B);
-        const int n = min(nbt - win_p0, kBtCache);
-        for (int i = tid; i < n; i += kPfWaves * 64) bt_s[i] = bt[win_p0 + i];
+    // One pair: wait for its stage, start the next pair's DMA into the other
+    // stage, multiply this wave's block of the pair.
+    auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
+        __syncthreads();  // cur's DMA landed (every wave waited for its own); nxt is free
+        if (pr + 1 < npairs) {
+            if (2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
+                load_window(2 * (pr + 1));
+                __syncthreads();
+            }
+            issue_pair(nxt, pr + 1);
+        }
+        if (2 * pr + kp < nkb)
+            compute(cur + kp * LY::BLOCK_BYTES, cur + (2 + kp) * LY::BLOCK_BYTES,
+                    (2 * pr + kp) * kKeyBlock);
     };
+
     load_window(0);
     __syncthreads();
-    if (nkb > 0)
-        st0.fetch(0, bt_s, win_p0, nbt, key_cache, value_cache, block_elems, num_blocks);
-    if (nkb > 1)
-        st1.fetch(kKeyBlock, bt_s, win_p0, nbt, key_cache, value_cache, block_elems,
-                  num_blocks);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        const int key0 = kb * kKeyBlock;
-        if (kb == next_win) {  // every thread's fetch from the old window is issued
-            load_window(kb);
-            next_win += kWinBlocks;
-        }
-        st0.stash(lds, lds + 2 * KS_ELEMS, key0, kend);
-        if (kb + 1 < nkb)
-            st1.stash(lds + KS_ELEMS, lds + 2 * KS_ELEMS + VT_ELEMS, key0 + kKeyBlock, kend);
-        __syncthreads();
-        if (kb + 2 < nkb)
-            st0.fetch(key0 + 2 * kKeyBlock, bt_s, win_p0, nbt, key_cache, value_cache, block_elems,
-                      num_blocks);
-        if (kb + 3 < nkb)
-            st1.fetch(key0 + 3 * kKeyBlock, bt_s, win_p0, nbt, key_cache, value_cache, block_elems,
-                      num_blocks);
-        if (kb + kp < nkb)
-            compute(lds + kp * KS_ELEMS, lds + 2 * KS_ELEMS + kp * VT_ELEMS, key0 + kp * kKeyBlock);
-        __syncthreads();
+    if (npairs > 0) issue_pair(stage_a, 0);
+    for (int pr = 0; pr < npairs; pr += 2) {
+        step(stage_a, stage_b, pr);
+        if (pr + 1 < npairs) step(stage_b, stage_a, pr + 1);
     }
+    __syncthreads();  // every wave is done with both stages
 
     // ---- merge the two key parities, normalise, store ------------------------
     // Each lane of an odd wave hands its (max, sum, O^T fragment) to the lane
     // of the even wave with the same rows; both use the same lane layout.
-    float *mo = (float *)smem + (size_t)rg * 64 * (DT * RT * 4 + 2 * RT);
-    float *my = mo + lane * (DT * RT * 4 + 2 * RT);
+    static_assert(4 * 64 * DT * RT * 4 * 4 <= LY::STAGE_BYTES, "merge area");
+    float *mo = (float *)stage_a + ((size_t)rg * 64 + lane) * (DT * RT * 4);
+    float *mml = (float *)stage_b + ((size_t)rg * 64 + lane) * (2 * RT);
     float lsum[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) lsum[rt] = __shfl(acc_l[rt][0], l16);  // row l16's sum
@@ -388,17 +403,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *(floatx4_v *)(my + (rt * DT + dt) * 4) = acc_o[dt][rt];
-            my[DT * RT * 4 + 2 * rt] = m_row[rt];
-            my[DT * RT * 4 + 2 * rt + 1] = lsum[rt];
+            for (int dt = 0; dt < DT; ++dt) *(floatx4_v *)(mo + (rt * DT + dt) * 4) = acc_o[dt][rt];
+            mml[2 * rt] = m_row[rt];
+            mml[2 * rt + 1] = lsum[rt];
         }
     }
     __syncthreads();
     if (kp == 1) return;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const float m1 = my[DT * RT * 4 + 2 * rt], l1 = my[DT * RT * 4 + 2 * rt + 1];
+        const float m1 = mml[2 * rt], l1 = mml[2 * rt + 1];
         const float M = fmaxf(m_row[rt], m1);
         const float f0 = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - M);
         const float f1 = (m1 == NEG_INF) ? 0.f : fast_exp2(m1 - M);
@@ -410,7 +424,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
         bf16_t *orow = out + ((int64_t)(q_begin + q0 + qi) * num_q_heads + g * G + hh) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const floatx4_v o1 = *(const floatx4_v *)(my + (rt * DT + dt) * 4);
+            const floatx4_v o1 = *(const floatx4_v *)(mo + (rt * DT + dt) * 4);
             const floatx4_v o = (acc_o[dt][rt] * f0 + o1 * f1) * inv;
             uint2 v;
             v.x = pack_bf16x2(o[0], o[1]);
