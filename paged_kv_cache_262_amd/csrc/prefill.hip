@@ -22,7 +22,9 @@
 // Staging.  Key blocks are gathered through the block table straight from
 // HBM into LDS (global_load_lds_dwordx4: each lane moves 16 bytes, no
 // registers), one pair of blocks ahead of the pair being multiplied, in two
-// LDS stages that alternate.  K and V rows keep their memory layout
+// LDS stages that alternate; the even-parity waves issue their share of it
+// before their products, the odd-parity ones after their softmax, so the
+// memory pipeline moves it while the matrix cores work.  K and V rows keep their memory layout
 // [key][dim]; the 16-byte chunks of each row are permuted by an XOR with a
 // function of the key so that the matrix-operand reads below hit distinct
 // LDS banks.  The block-table entries of the tile sit in an LDS window.
@@ -48,7 +50,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kPfWaves = 8;         // waves per workgroup (2 per SIMD)
+constexpr int kPfWaves = 8;         // waves per workgroup: 2 key parities x 4 row groups
 constexpr int kPfRows = 128;        // rows (query x head) per workgroup
 constexpr int kKeyBlock = 64;       // keys per LDS block
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
@@ -136,10 +138,11 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     constexpr int QT = kPfRows / G;  // queries per tile
     constexpr int KS = D / 32;       // k-steps of S^T = K Q^T
     constexpr int DT = D / 16;       // 16-dim tiles of O^T
-    constexpr int RT = 2;            // 16-row tiles per wave (32 rows)
+    constexpr int NRG = kPfWaves / 2;           // row groups
+    constexpr int RT = kPfRows / (16 * NRG);    // 16-row tiles per wave
     constexpr int ROWB = LY::ROWB;
     constexpr float NEG_INF = -__builtin_inff();
-    static_assert(kPfWaves == 8 && kPfRows == 4 * RT * 16, "4 row groups x 2 key parities");
+    static_assert(kPfRows == NRG * RT * 16, "row groups x 2 key parities");
 
     // Two stages in two distinct LDS arrays: the compiler then knows that the
     // operand reads of one stage do not wait for the DMA filling the other.
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int rg = w & 3, kp = w >> 2;  // row group, key parity
+    const int rg = w % NRG, kp = w / NRG;  // row group, key parity
 
     // ---- this lane's rows and their Q^T operands ----------------------------
     // Row r (0..127) of the tile = query r / G, head r % G of the group.
@@ -226,27 +229,51 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     // ---- DMA of one pair of key blocks into a stage -------------------------
     // The stage's 4 * SEGS segments of 1 KB ([K even][K odd][V even][V odd])
     // are split over the waves; lane i of a segment moves chunk i % NCH of row
-    // i / NCH.  Keys past kend read the row of key kend - 1 instead (data
-    // whose weight is exactly 0), so no LDS row is ever left stale.
+    // i / NCH.  The rows of a segment lie in one page, so the page lookup and
+    // the page address are wave-uniform (scalar).  In the tile's last block,
+    // keys past kend read the row of key kend - 1 instead (data whose weight
+    // is exactly 0), so no LDS row is ever left stale.
     const int seg_row = lane / LY::NCH, seg_ch = lane % LY::NCH;
-    auto issue_pair = [&](char *stage, int pr) __attribute__((always_inline)) {
-        const int key_pair0 = pr * 2 * kKeyBlock;
+    static_assert(B % LY::KPS == 0, "a segment's rows share a page");
+    static_assert(LY::SEGS_PER_WAVE <= 64, "one lane per segment");
+    // Lane j < SEGS_PER_WAVE looks up the page of the wave's segment j of pair
+    // pr, so all lookups of a pair cost one LDS round trip.
+    auto lookup_pages = [&](int pr) __attribute__((always_inline)) {
+        const int j = lane < LY::SEGS_PER_WAVE ? lane : 0;
+        const int seg = w * LY::SEGS_PER_WAVE + j;
+        const int kb = 2 * pr + ((seg / LY::SEGS) & 1);
+        const int key_s = min(kb * kKeyBlock + (seg % LY::SEGS) * LY::KPS, kend - 1);
+        return bt_s[key_s / B - win_p0];
+    };
+    // This wave's share of the DMA of pair pr into stage (seg_phys from
+    // lookup_pages(pr)).
+    auto issue_dma = [&](char *stage, int pr, int seg_phys) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < LY::SEGS_PER_WAVE; ++j) {
             const int seg = w * LY::SEGS_PER_WAVE + j;  // uniform
             const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1;
             const int s = seg % LY::SEGS;
-            if (2 * pr + bp >= nkb) continue;  // block past the tile's keys
+            const int kb = 2 * pr + bp;
+            if (kb >= nkb) continue;  // block past the tile's keys
+            const char *pool = (const char *)(tensor ? value_cache : key_cache);
+            lds_void *dst = (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024);
             const int kk = s * LY::KPS + seg_row;
-            const int key = min(key_pair0 + bp * kKeyBlock + kk, kend - 1);
-            const int phys = bt_s[key / B - win_p0];
-            const int64_t base = (phys >= 0 && (int64_t)phys < num_blocks)
-                                     ? (int64_t)phys * block_elems : 0;  // caller error: block 0
-            const bf16_t *src = (tensor ? value_cache : key_cache) + base +
-                                ((int64_t)g * B + key % B) * D + (seg_ch ^ LY::swz(kk)) * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const void *)src,
-                (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024), 16, 0, 0);
+            const int chunk_off = (seg_ch ^ LY::swz(kk)) << 4;
+            const int key_s = kb * kKeyBlock + s * LY::KPS;  // the segment's first key
+            if (kb * kKeyBlock + kKeyBlock <= kend) {
+                int phys = __builtin_amdgcn_readlane(seg_phys, j);
+                if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;  // caller error: block 0
+                const char *page = pool + ((int64_t)phys * block_elems + (int64_t)g * B * D) * 2;
+                const uint32_t off = (uint32_t)((key_s % B + seg_row) * ROWB + chunk_off);
+                __builtin_amdgcn_global_load_lds((const void *)(page + off), dst, 16, 0, 0);
+            } else {
+                const int key = min(key_s + seg_row, kend - 1);
+                int phys = bt_s[key / B - win_p0];
+                if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;
+                const char *src = pool + ((int64_t)phys * block_elems +
+                                          ((int64_t)g * B + key % B) * D) * 2 + chunk_off;
+                __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
+            }
         }
     };
 
@@ -265,7 +292,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
 
     // One 64-key block of this wave's parity: S^T = K Q^T, online softmax,
     // O^T += V^T P^T.
-    auto compute = [&](const char *Kb, const char *Vb, int key0) __attribute__((always_inline)) {
+    // dma_stage != nullptr: issue this wave's share of the DMA of pair
+    // dma_pair after the softmax, before the P V products.
+    auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
+                       int seg_phys) __attribute__((always_inline)) {
         floatx4_v s[4][RT];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -332,6 +362,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h) acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
         }
+        if (dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
         // O^T += V^T P^T, two dim tiles per batch; the transposing reads of
         // the next batch are in flight while the current one multiplies.
         const uint32_t vbase = lds_addr(Vb) + v_lane_off;
@@ -366,24 +397,32 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     };
 
     // One pair: wait for its stage, start the next pair's DMA into the other
-    // stage, multiply this wave's block of the pair.
+    // stage, multiply this wave's block of the pair.  The two waves of a SIMD
+    // have different parities: the even one issues its share of the DMA at
+    // once, the odd one after its softmax, so the memory pipeline drains one
+    // share while the other wave multiplies.
     auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
         __syncthreads();  // cur's DMA landed (every wave waited for its own); nxt is free
-        if (pr + 1 < npairs) {
+        const bool next = pr + 1 < npairs;
+        int seg_phys = 0;
+        if (next) {
             if (2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
                 load_window(2 * (pr + 1));
                 __syncthreads();
             }
-            issue_pair(nxt, pr + 1);
+            seg_phys = lookup_pages(pr + 1);
         }
-        if (2 * pr + kp < nkb)
+        const bool works = 2 * pr + kp < nkb;
+        const bool late = next && works && kp == 1;
+        if (next && !late) issue_dma(nxt, pr + 1, seg_phys);
+        if (works)
             compute(cur + kp * LY::BLOCK_BYTES, cur + (2 + kp) * LY::BLOCK_BYTES,
-                    (2 * pr + kp) * kKeyBlock);
+                    (2 * pr + kp) * kKeyBlock, late ? nxt : nullptr, pr + 1, seg_phys);
     };
 
     load_window(0);
     __syncthreads();
-    if (npairs > 0) issue_pair(stage_a, 0);
+    if (npairs > 0) issue_dma(stage_a, 0, lookup_pages(0));
     for (int pr = 0; pr < npairs; pr += 2) {
         step(stage_a, stage_b, pr);
         if (pr + 1 < npairs) step(stage_b, stage_a, pr + 1);
@@ -393,7 +432,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     // ---- merge the two key parities, normalise, store ------------------------
     // Each lane of an odd wave hands its (max, sum, O^T fragment) to the lane
     // of the even wave with the same rows; both use the same lane layout.
-    static_assert(4 * 64 * DT * RT * 4 * 4 <= LY::STAGE_BYTES, "merge area");
+    static_assert(NRG * 64 * DT * RT * 4 * 4 <= LY::STAGE_BYTES, "merge area");
     float *mo = (float *)stage_a + ((size_t)rg * 64 + lane) * (DT * RT * 4);
     float *mml = (float *)stage_b + ((size_t)rg * 64 + lane) * (2 * RT);
     float lsum[RT];
