@@ -2,12 +2,15 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
 A step is one pass of the hot path over one batch: the cache write of the
-step's new K/V tokens (pa_reshape_and_cache), then decode attention over every
-sequence's paged context (pa_decode_partitions + pa_decode_reduce), plus the
-prefill chunks when the workload has them (pa_prefill_chunk).  The default
-workload is the Llama-3-8B-shaped decode layer: 64 sequences, 32 q / 8 kv
-heads, head_dim 128, bf16, 16-token blocks, contexts uniform in [512, 4096],
-one new token per sequence.
+step's new K/V tokens, decode attention over every sequence's paged context
+(split-K partial results, then their merge), plus the prefill chunks when the
+workload has them (pa_prefill_chunk).  When the new tokens are one per
+sequence at its last position (a plain decode step) the cache write runs inside
+the decode pass (pa_decode_append_partitions + pa_decode_reduce); otherwise it
+is its own launch (pa_reshape_and_cache).  The default workload is the
+Llama-3-8B-shaped decode layer: 64 sequences, 32 q / 8 kv heads, head_dim 128,
+bf16, 16-token blocks, contexts uniform in [512, 4096], one new token per
+sequence.
 
 Inputs are synthetic (seeded) and already resident in HBM when timing starts.
 Steps alternate between independent replicas of the pools so that the 256 MB
@@ -57,6 +60,21 @@ def parse():
     return ap.parse_args()
 
 
+def fused_append(case) -> bool:
+    """A decode-only step whose new tokens are one per sequence, each at position
+    L - 1 of its sequence: the cache write then runs inside the decode pass
+    (pa_decode_append) instead of as its own launch."""
+    if case.num_chunks or case.slot_mapping.numel() != case.num_seqs:
+        return False
+    B = case.block_size
+    lens = case.context_lens.tolist()
+    if min(lens) <= 0:
+        return False
+    bt = case.block_tables
+    want = [int(bt[s, (L - 1) // B]) * B + (L - 1) % B for s, L in enumerate(lens)]
+    return want == case.slot_mapping.tolist()
+
+
 class Replica:
     """One device copy of a workload."""
 
@@ -70,6 +88,10 @@ class Replica:
         self.nv = case.new_value.to(dev)
         self.slots = case.slot_mapping.to(dev)
         self.out = torch.empty_like(self.q)
+        if fused_append(case):
+            S, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
+            self.nk_seq = case.new_key.reshape(S, Hkv, D).to(dev)
+            self.nv_seq = case.new_value.reshape(S, Hkv, D).to(dev)
         if case.num_chunks:
             self.cq = case.chunk_query.to(dev)
             self.cbt = case.chunk_block_tables.to(dev)
@@ -122,17 +144,23 @@ def main():
 
     ev = {k: [] for k in ("cw0", "cw1", "dp0", "dp1", "dr1", "pf0", "pf1")}
 
+    fused = fused_append(case)
+
     def step(i, record):
         r = reps[i % len(reps)]
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw0"].append(e)
-        if T:
+        if T and not fused:
             binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw1"].append(e)
             ev["dp0"].append(e)
-        binding.decode_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL, P, ws,
-                                  stream=stream)
+        if fused:
+            binding.decode_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
+                                             r.lens, case.scale, maxL, P, ws, stream=stream)
+        else:
+            binding.decode_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL, P,
+                                      ws, stream=stream)
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dp1"].append(e)
         binding.decode_reduce(r.out, r.lens, Hkv, B, case.max_blocks_per_seq, maxL, P, ws,
@@ -191,7 +219,9 @@ def main():
     t_pf = avg_ms("pf0", "pf1") if chunks else 0.0
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    dp_gbs = dec_bytes / (t_dp * 1e-3) / 1e9
+    # The fused step's decode kernel also moves the new tokens' rows.
+    dp_bytes = dec_bytes + (cw_bytes if fused else 0)
+    dp_gbs = dp_bytes / (t_dp * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -210,6 +240,8 @@ def main():
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
+            "cache_write": ("fused into the decode pass (pa_decode_append)" if fused
+                            else "pa_reshape_and_cache" if T else "none"),
             "replicas": len(reps),
             "prefill_chunks": chunks,
         },
@@ -226,7 +258,7 @@ def main():
             "unit": "GB/s",
             "frac": round(dp_gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "algorithmic_bytes_per_launch": dec_bytes,
+            "algorithmic_bytes_per_launch": dp_bytes,
         },
     }
     if chunks:
@@ -236,7 +268,7 @@ def main():
                                       "unit": "TFLOP/s",
                                       "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                                       "algorithmic_flops_per_launch": pf_flops}
-    if T:
+    if T and not fused:
         result["cache_write"] = {"ms": round(t_cw, 5), "bytes": cw_bytes,
                                  "GB/s": round(cw_bytes / (t_cw * 1e-3) / 1e9, 1)}
 

@@ -34,13 +34,15 @@
  *   - Device-side data are not validated on the host (that would need a
  *     synchronising copy).  Kernels stay inside the buffers whatever the
  *     data: a block-table entry outside [0, num_blocks) makes those tokens
- *     count as absent, a slot outside [0, num_blocks * block_size) is skipped,
- *     and context lengths are clamped to max_blocks_per_seq * block_size.
+ *     count as absent in decode (prefill reads block 0 in its place), a slot
+ *     outside [0, num_blocks * block_size) is skipped, and context lengths are
+ *     clamped to max_context_len (and to max_blocks_per_seq * block_size).
  *     Such inputs are caller errors and their results are unspecified.
  *   - Supported: dtype PA_F32 or PA_BF16 (prefill: PA_BF16 only), head_dim
  *     64 or 128, block_size 16 or 32, num_q_heads / num_kv_heads in
  *     {1, 2, 4, 8}.  Other shapes return PA_ERR_UNSUPPORTED.
- *   - All pointers must be 16-byte aligned (PA_ERR_INVALID_ARG otherwise).
+ *   - All pointers must be 16-byte aligned (PA_ERR_INVALID_ARG otherwise);
+ *     the decode workspace 256-byte aligned (PA_ERR_WORKSPACE otherwise).
  *   - Entry points are reentrant; concurrent calls on different streams must
  *     not share output or workspace buffers.
  */
@@ -97,17 +99,19 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
                                void *stream);
 
 /*
- * Partition size (tokens of one sequence handled by one workgroup) that
- * pa_decode uses when called with partition_size == 0.  A multiple of
- * block_size.
+ * Partition size that the fixed-partition decode path would pick for this
+ * batch (tokens of one sequence per workgroup, a multiple of 16); a
+ * convenience for callers that pass an explicit partition_size.  pa_decode
+ * itself treats partition_size == 0 as the balanced split described below.
  */
 int32_t pa_decode_auto_partition_size(int32_t num_seqs, int32_t num_kv_heads,
                                       int32_t max_context_len, int32_t block_size);
 
 /*
- * Bytes of device workspace pa_decode needs (0 is never returned for valid
- * input; a small minimum is always asked).  partition_size 0 = automatic,
- * resolved exactly as pa_decode resolves it.
+ * Bytes of device workspace pa_decode (and pa_decode_append) needs for these
+ * arguments, planned exactly as pa_decode plans them (0 is never returned; a
+ * small minimum is always asked).  The workspace must be 256-byte aligned;
+ * its contents need no initialisation and are scratch between calls.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
@@ -127,12 +131,21 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * be in the cache already (pa_reshape_and_cache first), so it is at position
  * context_lens[s] - 1.
  *
- * Each sequence is split into partitions of partition_size tokens (0 =
- * automatic); partitions are reduced by a second kernel through the
- * workspace (fp32 running max, sum and unnormalised output per partition).
+ * Split of the work (split-K over the context): the keys of every (sequence,
+ * kv head) are cut into units of 16 tokens.
+ *   partition_size == 0 and num_seqs <= 8192: balanced split.  All units of
+ *     the batch are dealt to a fixed number of waves in equal contiguous
+ *     ranges, whatever the mix of context lengths; a (sequence, kv head)
+ *     that spans several waves leaves one partial result per wave.
+ *   partition_size > 0 (a multiple of block_size and of 16, at most 4096),
+ *     or more than 8192 sequences: fixed partitions of partition_size tokens
+ *     (automatic size for partition_size == 0), one workgroup each.
+ * Partial results (fp32 running max, sum and unnormalised output) go through
+ * the workspace and a second kernel merges them with log-sum-exp rescaling.
  * max_context_len must be >= every context_lens[s]; it sizes the launch.
  * Inputs are bf16 or fp32; arithmetic is fp32; out is written in dtype
- * (bf16 by round-to-nearest-even).
+ * (bf16 by round-to-nearest-even).  The result does not depend on the split
+ * beyond fp32 rounding.
  */
 pa_status pa_decode(void *out, const void *query, const void *key_cache,
                     const void *value_cache, const int32_t *block_tables,
@@ -164,6 +177,47 @@ pa_status pa_decode_reduce(void *out, const int32_t *context_lens, int32_t num_s
                            int32_t block_size, int32_t max_blocks_per_seq,
                            int32_t max_context_len, int32_t partition_size, int32_t dtype,
                            const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_append -- one decode step with its new tokens: the cache write of
+ * pa_reshape_and_cache and pa_decode in one pass.
+ *
+ * For every sequence s with 0 < context_lens[s] <= max_context_len, the new
+ * token's rows new_key[s][:][:] and new_value[s][:][:] ([num_seqs]
+ * [num_kv_heads][head_dim]) are written bit for bit into the slot of position
+ * context_lens[s] - 1, i.e. block block_tables[s][(L - 1) / block_size] at
+ * offset (L - 1) % block_size, and then the same attention as pa_decode is
+ * computed over positions 0 .. L - 1, the new token included.  The result and
+ * the pools afterwards equal pa_reshape_and_cache with those slots followed by
+ * pa_decode.  With the balanced split the wave that reads the new token's
+ * unit writes it and uses it from registers, so no extra launch is needed.
+ *
+ * The block holding the new token must not be shared with another sequence
+ * of the batch (copy it first, as for any write into a shared block).
+ * Arguments as pa_decode, plus new_key and new_value (read).
+ */
+pa_status pa_decode_append(void *out, const void *query, const void *new_key,
+                           const void *new_value, void *key_cache, void *value_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
+                           float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * The first phase of pa_decode_append (the cache write and the partial
+ * results); pa_decode_reduce with the same arguments completes it.
+ */
+pa_status pa_decode_append_partitions(void *out, const void *query, const void *new_key,
+                                      const void *new_value, void *key_cache, void *value_cache,
+                                      const int32_t *block_tables, const int32_t *context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t max_context_len,
+                                      int32_t partition_size, float scale, int32_t dtype,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pa_prefill_chunk -- a chunk of consecutive prompt tokens attends causally to

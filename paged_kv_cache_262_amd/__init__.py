@@ -9,6 +9,8 @@ library is missing every entry point raises.
 from .binding import (  # noqa: F401
     PAError,
     decode,
+    decode_append,
+    decode_append_partitions,
     decode_partitions,
     decode_reduce,
     decode_workspace_bytes,

@@ -38,6 +38,11 @@ SIGNATURES = {
                                     _i32, _i64, _i32, _i32, _f, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _vp, _sz, _vp]),
+    "pa_decode_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                _i32, _i32, _i64, _i32, _i32, _f, _i32, _vp, _sz, _vp]),
+    "pa_decode_append_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                           _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f, _i32,
+                                           _vp, _sz, _vp]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
 }
@@ -178,6 +183,40 @@ def decode_reduce(out, context_lens, num_kv_heads, block_size, max_blocks_per_se
         _dev(out, "out"), _dev(context_lens, "context_lens"), S, Hq, num_kv_heads, D, block_size,
         max_blocks_per_seq, int(max_context_len), int(partition_size), _dtype(out),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                 context_lens, max_context_len, partition_size, scale, workspace):
+    d = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                     max_context_len, partition_size, scale, workspace)
+    S, Hkv, D = query.shape[0], key_cache.shape[1], query.shape[2]
+    for t, name in ((new_key, "new_key"), (new_value, "new_value")):
+        if tuple(t.shape) != (S, Hkv, D) or t.dtype != query.dtype:
+            raise ValueError(f"{name} must be [{S}, {Hkv}, {D}] {query.dtype}")
+    return d[:2] + (_dev(new_key, "new_key"), _dev(new_value, "new_value")) + d[2:]
+
+
+def decode_append(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                  context_lens, scale, max_context_len, partition_size=0, workspace=None,
+                  stream=None):
+    """One decode step with its new tokens: writes new_key/new_value [S, Hkv, D] at
+    position context_lens[s] - 1 of each sequence and attends over it; writes ``out``."""
+    if workspace is None:
+        workspace = make_workspace(query, key_cache, max_context_len, partition_size)
+    _check(load().pa_decode_append(*_append_args(out, query, new_key, new_value, key_cache,
+                                                 value_cache, block_tables, context_lens,
+                                                 max_context_len, partition_size, scale,
+                                                 workspace), _stream(stream)))
+    return out
+
+
+def decode_append_partitions(out, query, new_key, new_value, key_cache, value_cache,
+                             block_tables, context_lens, scale, max_context_len, partition_size,
+                             workspace, stream=None):
+    _check(load().pa_decode_append_partitions(
+        *_append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                      context_lens, max_context_len, partition_size, scale, workspace),
         _stream(stream)))
 
 

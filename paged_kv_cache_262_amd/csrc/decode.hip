@@ -63,6 +63,7 @@ constexpr int kBufferBudget = PA_BUFFER_BUDGET;  // VGPRs for q, accumulators an
 constexpr float NEG_INF = -__builtin_inff();
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: no memcpy
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a),
@@ -337,15 +338,22 @@ __device__ __forceinline__ int seq_of_unit(const int *scan, int S, int64_t u, in
     return lo;
 }
 
-template <typename T, int D, int B, int G, int NW>
+// AP (append): the step's new token of sequence s (rows new_key[s],
+// new_value[s], [S][Hkv][D]) sits at position L_s - 1.  The wave that streams
+// the unit holding that position writes the rows into their slot before it
+// loads the unit, so the write needs no ordering with any other wave: no other
+// wave reads that unit.
+template <typename T, int D, int B, int G, int NW, bool AP>
 __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
-    T *__restrict__ out, const T *__restrict__ query, const T *__restrict__ key_cache,
-    const T *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    T *__restrict__ out, const T *__restrict__ query, T *__restrict__ key_cache,
+    T *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int S, int num_q_heads, int num_kv_heads,
     int max_blocks, int max_tokens, int64_t num_blocks, int nw, float scale_log2,
-    float *__restrict__ rec_o, float *__restrict__ rec_ml, int *__restrict__ ws_scan) {
+    float *__restrict__ rec_o, float *__restrict__ rec_ml, int *__restrict__ ws_scan,
+    const T *__restrict__ new_key, const T *__restrict__ new_value) {
     using SH = DecodeShape<T, D, G>;
     constexpr int LPT = SH::LPT, CPL = SH::CPL, EPC = SH::EPC, ROWB = SH::ROWB;
+    constexpr int TPP = SH::TPP, NPASS = SH::NPASS;
     __shared__ int scan[kStreamMaxSeqs + 1];
     scan_units<NW>(scan, context_lens, S, max_tokens);
     const int Hkv = num_kv_heads;
@@ -407,25 +415,93 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     for (int64_t base = ua; base < ub; base += 64) {
         const int n = (int)min((int64_t)64, ub - base);
         // Lane k describes unit base + k: its pair, row count and block.
-        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0;
-        {
+        // With AP, l_new is the row of the unit that holds the new token
+        // (its last unit, when the length was not clamped), else -1.
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1;
+        int l_s = 0, l_j = 0, l_us = 1;
+        if (lane < n) {  // from the LDS scan alone
             const int64_t u = base + lane;
-            if (lane < n) {
-                const int s = seq_of_unit(scan, S, u, Hkv);
-                const int us = scan[s + 1] - scan[s];
-                const int rem = (int)(u - (int64_t)scan[s] * Hkv);
-                const int g = rem / us, j = rem - g * us;
-                const int L = clamp_len(context_lens[s], max_tokens);
-                const int tok = j * kUnitTokens;
-                l_item = s * Hkv + g;
-                l_nvalid = min(kUnitTokens, L - tok);
-                l_tokoff = tok % B;
-                const int phys = block_tables[(int64_t)s * max_blocks + tok / B];
-                if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
-                l_phys = phys;
+            l_s = seq_of_unit(scan, S, u, Hkv);
+            l_us = scan[l_s + 1] - scan[l_s];
+            const int rem = (int)(u - (int64_t)scan[l_s] * Hkv);
+            const int g = rem / l_us;
+            l_j = rem - g * l_us;
+            l_item = l_s * Hkv + g;
+        }
+        // Append: the new tokens of the pairs that end in this chunk go to
+        // their slots before this wave loads those units (its own stores
+        // precede its loads of the same bytes).  The lanes form groups of
+        // 2 * NCH, one 16-byte chunk of the K or V row each, one pair per
+        // group.  The rows of the first PE pairs are fetched together with the
+        // descriptors below, so they cost no extra round trip.
+        constexpr int NCH = ROWB / 16, PE = 64 / (2 * NCH);
+        const int grp = lane / (2 * NCH), c2 = lane % (2 * NCH);
+        const bool c2v = c2 >= NCH;
+        const int c2ch = c2v ? c2 - NCH : c2;
+        uint64_t ends = 0;
+        int first = -1;
+        u32x4 first_row = {0, 0, 0, 0};
+        if (AP) {
+            ends = __builtin_amdgcn_ballot_w64(lane < n && l_j == l_us - 1);
+#pragma unroll
+            for (int e = 0; e < PE; ++e) {
+                if (ends) {
+                    const int bit = (int)__builtin_ctzll(ends);
+                    ends &= ends - 1;
+                    if (grp == e) first = bit;
+                }
             }
+            const int it = __shfl(l_item, first < 0 ? 0 : first);
+            if (first >= 0)
+                first_row = *(const u32x4 *)((const char *)(c2v ? new_value : new_key) +
+                                             (int64_t)it * ROWB + c2ch * 16);
+        }
+        if (lane < n) {
+            const int Lraw = context_lens[l_s];
+            const int L = clamp_len(Lraw, max_tokens);
+            const int tok = l_j * kUnitTokens;
+            l_nvalid = min(kUnitTokens, L - tok);
+            l_tokoff = tok % B;
+            const int phys = block_tables[(int64_t)l_s * max_blocks + tok / B];
+            if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
+            l_phys = phys;
+            if (AP && Lraw == L && l_j == l_us - 1 && l_nvalid > 0) l_new = l_nvalid - 1;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
+
+        if (AP) {
+            // Store the row of pair unit `mine` (a lane index of this chunk).
+            auto put = [&](int mine, const u32x4 &row) __attribute__((always_inline)) {
+                const int src_lane = mine < 0 ? 0 : mine;
+                const int it = __shfl(l_item, src_lane), ph = __shfl(l_phys, src_lane);
+                const int to = __shfl(l_tokoff, src_lane), nr = __shfl(l_new, src_lane);
+                if (mine >= 0 && nr >= 0) {
+                    char *dst = (char *)(c2v ? value_cache : key_cache) + (int64_t)ph * block_bytes +
+                                (int64_t)(it % Hkv) * head_bytes + (int64_t)(to + nr) * ROWB +
+                                c2ch * 16;
+                    *(u32x4 *)dst = row;
+                }
+            };
+            put(first, first_row);
+            while (ends) {  // more pairs end in this chunk than one batch holds
+                int mine = -1;
+#pragma unroll
+                for (int e = 0; e < PE; ++e) {
+                    if (ends) {
+                        const int bit = (int)__builtin_ctzll(ends);
+                        ends &= ends - 1;
+                        if (grp == e) mine = bit;
+                    }
+                }
+                const int it = __shfl(l_item, mine < 0 ? 0 : mine);
+                u32x4 row = {0, 0, 0, 0};
+                if (mine >= 0)
+                    row = *(const u32x4 *)((const char *)(c2v ? new_value : new_key) +
+                                           (int64_t)it * ROWB + c2ch * 16);
+                put(mine, row);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
 
         // Unit i of the chunk, or an empty range past the current segment.
         auto locate = [&](int i, int seg_end, int &nvalid) __attribute__((always_inline)) -> UnitRes {
@@ -463,7 +539,8 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
                                ((int64_t)cur_s * num_q_heads + (int64_t)cur_g * G) * ROWB, r);
             }
 #pragma unroll
-            for (int b = 0; b < NB; ++b) load_unit(buf[b], locate(i0 + b, i1, nv[b]), lane_off);
+            for (int b = 0; b < NB; ++b)
+                load_unit(buf[b], locate(i0 + b, i1, nv[b]), lane_off);
             for (int i = i0; i < i1; i += NB) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -724,13 +801,30 @@ template <typename T, int D, int B, int G>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
     if (a.stream_waves > 0) {
         dim3 grid(cdiv(a.stream_waves, kDecodeWaves));
-        hipLaunchKernelGGL((decode_stream_kernel<T, D, B, G, kDecodeWaves>), grid,
-                           dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
-                           (const T *)a.key_cache, (const T *)a.value_cache, a.block_tables,
-                           a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
-                           a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
-                           a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan);
+        if (a.new_key)
+            hipLaunchKernelGGL((decode_stream_kernel<T, D, B, G, kDecodeWaves, true>), grid,
+                               dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
+                               (T *)a.key_cache, (T *)a.value_cache, a.block_tables,
+                               a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
+                               a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                               a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan, (const T *)a.new_key,
+                               (const T *)a.new_value);
+        else
+            hipLaunchKernelGGL((decode_stream_kernel<T, D, B, G, kDecodeWaves, false>), grid,
+                               dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
+                               (T *)a.key_cache, (T *)a.value_cache, a.block_tables,
+                               a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
+                               a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                               a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan, (const T *)nullptr,
+                               (const T *)nullptr);
     } else {
+        if (a.new_key) {
+            const hipError_t e = launch_append_rows(
+                a.new_key, a.new_value, (void *)a.key_cache, (void *)a.value_cache, a.block_tables,
+                a.context_lens, a.num_seqs, a.num_kv_heads, D, B, a.max_blocks_per_seq,
+                a.num_blocks, max_tokens(a), (int)sizeof(T), stream);
+            if (e != hipSuccess) return e;
+        }
         dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
         hipLaunchKernelGGL((decode_partition_kernel<T, D, B, G, kDecodeWaves>), grid,
                            dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,

@@ -172,6 +172,8 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
     a.stream_waves = plan.stream ? plan.waves : 0;
     a.scale = scale;
     a.dtype = dtype;
+    a.new_key = nullptr;
+    a.new_value = nullptr;
     char *ws = (char *)workspace;
     a.ws_o = uses_ws ? (float *)ws : nullptr;
     a.ws_ml = uses_ws ? (float *)(ws + plan.o_bytes) : nullptr;
@@ -297,6 +299,50 @@ pa_status pa_decode(void *out, const void *query, const void *key_cache,
     s = hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream), "decode_partitions");
     if (s != PA_OK) return s;
     return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
+}
+
+pa_status pa_decode_append_partitions(void *out, const void *query, const void *new_key,
+                                      const void *new_value, void *key_cache, void *value_cache,
+                                      const int32_t *block_tables, const int32_t *context_lens,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, int32_t max_context_len,
+                                      int32_t partition_size, float scale, int32_t dtype,
+                                      void *workspace, size_t workspace_bytes, void *stream) {
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, query, key_cache, value_cache, block_tables,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                               partition_size, scale, dtype, workspace, workspace_bytes, true);
+    if (s != PA_OK) return s;
+    if (num_seqs > 0) {
+        CHECK_PTR(new_key, 16);
+        CHECK_PTR(new_value, 16);
+    }
+    st.a.new_key = new_key;
+    st.a.new_value = new_value;
+    return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
+                      "decode_append_partitions");
+}
+
+pa_status pa_decode_append(void *out, const void *query, const void *new_key,
+                           const void *new_value, void *key_cache, void *value_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int64_t num_blocks, int32_t max_context_len, int32_t partition_size,
+                           float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    pa_status s = pa_decode_append_partitions(
+        out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        num_blocks, max_context_len, partition_size, scale, dtype, workspace, workspace_bytes,
+        stream);
+    if (s != PA_OK) return s;
+    return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, max_context_len, partition_size,
+                            dtype, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,

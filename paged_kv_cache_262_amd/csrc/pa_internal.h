@@ -13,6 +13,17 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *ke
                                     int block_size, int64_t num_blocks, int elem_bytes,
                                     hipStream_t stream);
 
+// Writes the new token of each sequence s (rows key[s], value[s], [S][Hkv][D])
+// into the slot of position context_lens[s] - 1; sequences whose length is 0
+// or above max_tokens, or whose block-table entry is outside the pool, are
+// skipped.
+hipError_t launch_append_rows(const void *key, const void *value, void *key_cache,
+                              void *value_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, int num_seqs, int num_kv_heads,
+                              int head_dim, int block_size, int max_blocks_per_seq,
+                              int64_t num_blocks, int max_tokens, int elem_bytes,
+                              hipStream_t stream);
+
 // Largest batch the balanced (stream) decode split handles: its workgroups
 // scan the per-sequence unit counts in LDS.  Larger batches use fixed
 // partitions.
@@ -38,6 +49,9 @@ struct DecodeArgs {
     float *ws_o;
     float *ws_ml;
     int *ws_scan;
+    // Non-null: the step's new token of each sequence ([S][Hkv][D]) is written
+    // at position context_lens[s] - 1 and attended to (decode with append).
+    const void *new_key, *new_value;
 };
 
 // Returns hipErrorNotSupported when no kernel is built for the shape.

@@ -1,0 +1,142 @@
+"""GPU parity of the fused decode step (pa_decode_append) through the C ABI.
+
+pa_decode_append must leave the pools bit-identical to the oracle's cache
+write of each sequence's new token at position L - 1, and its output must
+match the fp64 oracle decode over those pools (1e-5 abs + rel for fp32,
+1e-2 abs + 2e-2 rel for bf16).  It is also compared bit for bit with the
+unfused pair pa_reshape_and_cache + pa_decode, which does the same
+arithmetic in the same order.
+"""
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_262_amd import binding
+from paged_kv_cache_262_amd import workloads as W
+from tests.gpu_util import check_close, dev, oracle_decode, oracle_pools, say
+
+pytestmark = pytest.mark.gpu
+
+
+def per_sequence_rows(case):
+    """new_key / new_value as [S, Hkv, D]: the case holds one row per sequence
+    with L > 0 (in sequence order); sequences with L == 0 get zero rows."""
+    S, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
+    nk = torch.zeros((S, Hkv, D), dtype=case.new_key.dtype)
+    nv = torch.zeros_like(nk)
+    t = 0
+    for s, L in enumerate(case.context_lens.tolist()):
+        if L > 0:
+            nk[s], nv[s] = case.new_key[t], case.new_value[t]
+            t += 1
+    assert t == case.new_key.shape[0]
+    return nk, nv
+
+
+def run_append(case, partition_size=0, split=False):
+    nk, nv = per_sequence_rows(case)
+    kc, vc = dev(case.key_cache), dev(case.value_cache)
+    q = dev(case.query)
+    out = torch.empty_like(q)
+    maxL = max(1, int(case.context_lens.max()))
+    bt, lens = dev(case.block_tables), dev(case.context_lens)
+    if split:
+        ws = binding.make_workspace(q, kc, maxL, partition_size)
+        binding.decode_append_partitions(out, q, dev(nk), dev(nv), kc, vc, bt, lens, case.scale,
+                                         maxL, partition_size, ws)
+        binding.decode_reduce(out, lens, case.num_kv_heads, case.block_size,
+                              case.block_tables.shape[1], maxL, partition_size, ws)
+    else:
+        binding.decode_append(out, q, dev(nk), dev(nv), kc, vc, bt, lens, case.scale, maxL,
+                              partition_size=partition_size)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+def check_case(case, what, partition_size=0, split=False):
+    say("append", what, "P", partition_size, "split", split)
+    out, kc, vc = run_append(case, partition_size, split)
+    rk, rv = oracle_pools(case)
+    assert torch.equal(kc.cpu().view(torch.uint8), rk.view(torch.uint8)), f"{what}: K pool"
+    assert torch.equal(vc.cpu().view(torch.uint8), rv.view(torch.uint8)), f"{what}: V pool"
+    ref = oracle_decode(case, rk, rv)
+    check_close(out, ref, case.dtype, what)
+    return out
+
+
+SHAPES = [(dt, D, B, G) for dt in ("f32", "bf16") for D in (64, 128) for B in (16, 32)
+          for G in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("dtype,D,B,G", SHAPES)
+def test_append_parity_shapes(dtype, D, B, G):
+    Hkv = 2
+    gen = torch.Generator().manual_seed(2000 + D + B + G)
+    lens = [0, 1, B - 1, B, B + 1, 16, 17, 64, 65, 257, 700] + \
+        [int(x) for x in torch.randint(1, 1100, (3,), generator=gen)]
+    c = W.make_case("append", 11, dtype, Hkv * G, Hkv, D, B, lens,
+                    new_positions=[L - 1 if L else None for L in lens], extra_blocks=2)
+    for P in (0, 64):
+        out = check_case(c, f"{dtype} D{D} B{B} G{G}", partition_size=P)
+        assert (out[0] == 0).all()                  # empty context: zeros, nothing written
+
+
+def test_append_many_short_sequences():
+    """Hundreds of 1..40-token sequences: many pairs end inside one wave's
+    64-unit chunk, so the slot writes go in several batches."""
+    c = W.random_case(77, "bf16", 300, 8, 2, 128, 16, 1, 40, extra_blocks=5)
+    check_case(c, "short seqs bf16")
+    c = W.random_case(78, "f32", 200, 4, 4, 64, 32, 1, 40, extra_blocks=5)
+    check_case(c, "short seqs f32")
+
+
+def test_append_llama8b_matches_unfused_bitwise():
+    """The Llama-3-8B-shaped step: fused output and pools equal the unfused
+    cache write + decode bit for bit, and the oracle within tolerance."""
+    c = W.NAMED["llama8b_decode"]()
+    fused = check_case(c, "llama8b fused")
+    split = check_case(c, "llama8b split phases", split=True)
+    kc, vc = dev(c.key_cache), dev(c.value_cache)
+    binding.reshape_and_cache(dev(c.new_key), dev(c.new_value), kc, vc, dev(c.slot_mapping))
+    q = dev(c.query)
+    ref = torch.empty_like(q)
+    binding.decode(ref, q, kc, vc, dev(c.block_tables), dev(c.context_lens), c.scale,
+                   int(c.context_lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(split.view(torch.int16), ref.view(torch.int16))
+
+
+def test_append_one_hot_new_token_dominates():
+    """The new token alone carries a huge logit, so each output row must equal
+    the new token's V row exactly: proof that the kernel attends to the row it
+    wrote, not to what the pool held at that slot before."""
+    c = W.random_case(91, "bf16", 40, 8, 2, 128, 16, 1, 300, extra_blocks=3)
+    nk, nv = per_sequence_rows(c)
+    q = torch.zeros_like(c.query)
+    q[:, :, 0] = 100.0
+    nk.zero_()
+    nk[:, :, 0] = 100.0                              # logit 100*100*scale ~ 884 above the rest
+    kcache = c.key_cache.clone()
+    kcache[..., 0] = 0.0                             # every cached key: logit 0
+    c.query, c.key_cache = q.to(c.query.dtype), kcache
+    kc, vc = dev(c.key_cache), dev(c.value_cache)
+    out = torch.empty_like(dev(c.query))
+    maxL = int(c.context_lens.max())
+    say("append one-hot")
+    binding.decode_append(out, dev(c.query), dev(nk), dev(nv), kc, vc, dev(c.block_tables),
+                          dev(c.context_lens), c.scale, maxL)
+    torch.cuda.synchronize()
+    G = c.num_q_heads // c.num_kv_heads
+    expect = nv.repeat_interleave(G, dim=1)          # [S, Hq, D]
+    assert torch.equal(out.cpu().view(torch.int16), expect.view(torch.int16))
+
+
+def test_append_rejects_bad_rows():
+    c = W.random_case(5, "bf16", 4, 8, 2, 128, 16, 1, 50)
+    q = dev(c.query)
+    kc, vc = dev(c.key_cache), dev(c.value_cache)
+    bad = torch.zeros((3, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        binding.decode_append(torch.empty_like(q), q, bad, bad, kc, vc, dev(c.block_tables),
+                              dev(c.context_lens), c.scale, 50)
