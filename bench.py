@@ -22,6 +22,7 @@ bandwidth: algorithmic KV bytes of the step / step time.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -58,6 +59,35 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     return ap.parse_args()
+
+
+# Sources each kernel is built from; the traffic figures in
+# profiles/hbm_traffic.txt are only reported while these are unchanged.
+KERNEL_SOURCES = {
+    "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
+    "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
+    "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
+}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a copy of known size), or None if not measured on these sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "paged_kv_cache_262_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) >= 4 and not line.startswith("#") and parts[:3] == [kernel, workload,
+                                                                               digest]:
+                return int(parts[3])
+    return None
 
 
 def fused_append(case) -> bool:
@@ -219,6 +249,8 @@ def main():
     t_pf = avg_ms("pf0", "pf1") if chunks else 0.0
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    dp_kernel = ("decode_stream_kernel"
+                 if P == 0 and S <= 8192 else "decode_partition_kernel")
     # The fused step's decode kernel also moves the new tokens' rows.
     dp_bytes = dec_bytes + (cw_bytes if fused else 0)
     dp_gbs = dp_bytes / (t_dp * 1e-3) / 1e9
@@ -251,13 +283,13 @@ def main():
         "kernels_ms": {"reshape_and_cache": round(t_cw, 5), "decode_partition": round(t_dp, 5),
                        "decode_reduce": round(t_dr, 5), "prefill_chunk": round(t_pf, 5)},
         "roofline": {
-            "kernel": "decode_stream_kernel" if P == 0 else "decode_partition_kernel",
+            "kernel": dp_kernel,
             "bound": "hbm",
             "achieved": round(dp_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dp_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dp_kernel, case.name),
             "algorithmic_bytes_per_launch": dp_bytes,
         },
     }
@@ -267,6 +299,8 @@ def main():
                                       "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                       "unit": "TFLOP/s",
                                       "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "traffic": measured_traffic("prefill_chunk_kernel",
+                                                                  case.name),
                                       "algorithmic_flops_per_launch": pf_flops}
     if T and not fused:
         result["cache_write"] = {"ms": round(t_cw, 5), "bytes": cw_bytes,
