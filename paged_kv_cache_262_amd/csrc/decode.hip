@@ -65,6 +65,13 @@ constexpr float NEG_INF = -__builtin_inff();
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: no memcpy
 
+// fp32 pair -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float floatx2_t __attribute__((ext_vector_type(2)));
+    const floatx2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a),
                                            __builtin_bit_cast(bf16x2_v, b), c, false);
@@ -239,23 +246,62 @@ struct WaveAcc {
                 for (int i = 0; i < S::OPL; ++i) o[h][i] *= alpha;
             }
         }
+        if constexpr (std::is_same<T, bf16_t>::value) {
+            // bf16: the two passes pp, pp + 1 a lane holds are two tokens.
+            // Their weights are rounded to a bf16 pair (as the matrix-core
+            // prefill does) and the matching V elements of both tokens are
+            // packed into pairs, so one dot2 per head and element pair does
+            // the work of two FMAs.  The row sums use the same rounded
+            // weights, so numerator and denominator agree.
+            static_assert(NPASS % 2 == 0, "token pairs");
 #pragma unroll
-        for (int pp = 0; pp < NPASS; ++pp) {
-            float pr[G];
+            for (int pp = 0; pp < NPASS; pp += 2) {
+                uint32_t pk[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                pr[h] = fast_exp2(sc[pp][h] - m[h]);
-                l[h] += pr[h];
+                for (int h = 0; h < G; ++h) {
+                    pk[h] = pack_bf16x2(fast_exp2(sc[pp][h] - m[h]),
+                                        fast_exp2(sc[pp + 1][h] - m[h]));
+                    l[h] = dot2_bf16(pk[h], 0x3F803F80u, l[h]);  // + both rounded weights
+                }
+#pragma unroll
+                for (int k = 0; k < CPL; ++k) {
+                    const uint32_t a[4] = {R.v[pp][k].x, R.v[pp][k].y, R.v[pp][k].z,
+                                           R.v[pp][k].w};
+                    const uint32_t b[4] = {R.v[pp + 1][k].x, R.v[pp + 1][k].y, R.v[pp + 1][k].z,
+                                           R.v[pp + 1][k].w};
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const uint32_t lo = __builtin_amdgcn_perm(b[w2], a[w2], 0x05040100u);
+                        const uint32_t hi = __builtin_amdgcn_perm(b[w2], a[w2], 0x07060302u);
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            float &o0 = o[h][k * EPC + 2 * w2];
+                            float &o1 = o[h][k * EPC + 2 * w2 + 1];
+                            o0 = dot2_bf16(pk[h], lo, o0);
+                            o1 = dot2_bf16(pk[h], hi, o1);
+                        }
+                    }
+                }
             }
+        } else {
 #pragma unroll
-            for (int k = 0; k < CPL; ++k) {
-                float v[EPC];
-                chunk_widen<T>(R.v[pp][k], v);
+            for (int pp = 0; pp < NPASS; ++pp) {
+                float pr[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h)
+                for (int h = 0; h < G; ++h) {
+                    pr[h] = fast_exp2(sc[pp][h] - m[h]);
+                    l[h] += pr[h];
+                }
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e)
-                        o[h][k * EPC + e] = fmaf(pr[h], v[e], o[h][k * EPC + e]);
+                for (int k = 0; k < CPL; ++k) {
+                    float v[EPC];
+                    chunk_widen<T>(R.v[pp][k], v);
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e)
+                            o[h][k * EPC + e] = fmaf(pr[h], v[e], o[h][k * EPC + e]);
+                }
             }
         }
     }
