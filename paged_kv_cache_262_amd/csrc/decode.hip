@@ -40,6 +40,8 @@
 //     pair it touches.  The load is balanced whatever the mix of context
 //     lengths, waves never synchronise, and a pair that falls inside one wave
 //     is finished by that wave.
+//   - decode_stream_mma_kernel: the same split for bf16 with both products
+//     on the matrix cores (see its comment); the default for bf16.
 //   - decode_partition_kernel (an explicit partition size): one workgroup per
 //     (sequence, kv head, partition of P tokens), waves merged in LDS.
 #include <type_traits>
@@ -399,7 +401,6 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
     const T *__restrict__ new_key, const T *__restrict__ new_value) {
     using SH = DecodeShape<T, D, G>;
     constexpr int LPT = SH::LPT, CPL = SH::CPL, EPC = SH::EPC, ROWB = SH::ROWB;
-    constexpr int TPP = SH::TPP, NPASS = SH::NPASS;
     __shared__ int scan[kStreamMaxSeqs + 1];
     scan_units<NW>(scan, context_lens, S, max_tokens);
     const int Hkv = num_kv_heads;
@@ -592,6 +593,356 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
                 for (int b = 0; b < NB; ++b) {
                     if (nv[b] > 0) acc.process(buf[b], nv[b], scale_log2, tg);
                     load_unit(buf[b], locate(i + NB + b, i1, nv[b]), lane_off);
+                }
+            }
+            i0 = i1;
+        }
+    }
+    if (cur_item >= 0) finish();
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split on the matrix cores (bf16).
+//
+// With grouped-query attention the G query heads of a kv head meet the same
+// 16-token unit: per unit a G x 16 x D contraction for the logits and a
+// G x D x 16 one for the output.  Done on the vector ALUs (the kernel above)
+// that arithmetic is one fp32 operation per head per element, which at G = 8
+// takes longer than streaming the unit from HBM.  Here both products run on
+// MFMA, transposed so that the softmax weights pass from one to the other in
+// registers (as in the prefill kernel):
+//   S^T [16 tokens x 16 columns] = K [16 x D] . Q^T [D x 16]   (16x16x32, D/32 steps)
+//   O^T [D x 16 columns]        += V^T [D x 16] . P^T [16 x 16] (16x16x16, D/16 tiles)
+// Column c < G is query head c of the group (the others carry zeros).  K goes
+// from HBM straight into the A-operand registers; V goes by DMA into a LDS
+// slot of the wave and comes back transposed (ds_read_b64_tr_b16), 4 tokens
+// of one dim per lane.  The loads of a unit use buffer resources whose range
+// is the unit's valid rows, so rows past the context arrive as zeros.  The
+// work split, records and reduce are those of decode_stream_kernel.
+// ---------------------------------------------------------------------------
+
+constexpr int kMmaBuffers = 3;  // units in flight + 1 per wave
+constexpr int kMmaWaves = 4;    // waves per workgroup
+
+typedef __bf16 bf16x8_mv __attribute__((ext_vector_type(8)));
+typedef short s16x4_mv __attribute__((ext_vector_type(4)));
+typedef float f32x4_mv __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_mv;
+
+__device__ __forceinline__ s16x4_mv lds_tr16(uint32_t addr) {
+    s16x4_mv r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+// Completes the transposing reads above (and orders later memory operations,
+// the next DMA into the slot among them, after it).
+template <int N>
+__device__ __forceinline__ void lds_tr_wait(s16x4_mv (&v)[N]) {
+    static_assert(N == 4 || N == 8, "batch");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                       "+v"(v[6]), "+v"(v[7])
+                     : : "memory");
+}
+
+// Chunk permutation of a V row in its LDS slot: chunk c of row r sits at
+// c ^ mma_swz(r), so the transposing reads of 16 rows hit distinct banks.
+template <int D>
+__device__ __forceinline__ int mma_swz(int row) {
+    return D == 128 ? (row & 7) << 1 : ((row >> 1) & 3) << 1;
+}
+
+// 16 bytes per lane from a buffer (offset voff) into LDS at lds + 16 * lane;
+// lanes outside the buffer's range write zeros.
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_mv *)lds, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+__device__ __forceinline__ float max4_lanes(float x) {  // over lanes l, l^16, l^32, l^48
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int D, int B, int G, int NW, bool AP>
+__global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
+    bf16_t *__restrict__ out, const bf16_t *__restrict__ query, bf16_t *__restrict__ key_cache,
+    bf16_t *__restrict__ value_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int S, int num_q_heads, int num_kv_heads,
+    int max_blocks, int max_tokens, int64_t num_blocks, int nw, float scale_log2,
+    float *__restrict__ rec_o, float *__restrict__ rec_ml, int *__restrict__ ws_scan,
+    const bf16_t *__restrict__ new_key, const bf16_t *__restrict__ new_value) {
+    constexpr int ROWB = D * 2, NCH = ROWB / 16, KS = D / 32, DT = D / 16;
+    constexpr int UNIT_BYTES = kUnitTokens * ROWB, NB = kMmaBuffers;
+    constexpr int KPS = 1024 / ROWB;               // rows per 1 KB DMA segment
+    constexpr int SEGS = UNIT_BYTES / 1024;        // DMA instructions per unit
+    static_assert(G <= 16, "group fits the 16 columns");
+    extern __shared__ int scan[];                  // [S + 1], sized at launch
+    __shared__ __attribute__((aligned(1024))) char vslot[NW][NB][UNIT_BYTES];
+    scan_units<NW>(scan, context_lens, S, max_tokens);
+    const int Hkv = num_kv_heads;
+    const int64_t U = (int64_t)scan[S] * Hkv;
+    if (blockIdx.x == 0)
+        for (int s = threadIdx.x; s <= S; s += NW * 64) ws_scan[s] = scan[s];
+
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int nwe = (int)min((int64_t)nw, U);
+    const int gw = blockIdx.x * NW + w;
+    if (gw >= nwe) return;
+    const int64_t ua = U * gw / nwe, ub = U * (gw + 1) / nwe;
+
+    const int64_t head_bytes = (int64_t)B * ROWB;
+    const int64_t block_bytes = head_bytes * Hkv;
+    const char *kbase = (const char *)key_cache;
+    const char *vbase = (const char *)value_cache;
+
+    // Lane offsets.  K operand of k-step ks: token l16, dims ks * 32 + lg * 8.
+    const int k_off = l16 * ROWB + lg * 16;
+    // V DMA: lane i of segment sg moves chunk i % NCH of row sg * KPS + i / NCH,
+    // stored at chunk position (i % NCH) ^ swz(row) of that row.
+    const int dma_row = lane / NCH, dma_ch = lane % NCH;
+    // V^T operand of dim tile dt: the lanes of group lg read rows 4 * lg + (l16 >> 2),
+    // dims dt * 16 + 4 * (l16 & 3), i.e. chunk 2 * dt + ((l16 & 3) >> 1), half l16 & 1.
+    const int v_row = 4 * lg + (l16 >> 2);
+    const uint32_t v_lane =
+        v_row * ROWB + (l16 & 1) * 8 + ((mma_swz<D>(v_row) ^ ((l16 & 3) >> 1)) << 4);
+    // A operand whose row 0 is all ones (for the column sums of P^T).
+    const s16x4_mv ones_a = l16 == 0 ? s16x4_mv{0x3F80, 0x3F80, 0x3F80, 0x3F80} : s16x4_mv{0, 0, 0, 0};
+
+    u32x4 qt[KS];          // Q^T operand of the current pair
+    f32x4_mv acc_o[DT];    // O^T: lane holds dims dt * 16 + 4 * lg + i of column l16
+    f32x4_mv acc_l;        // element 0 of lanes 0..15: sum of weights of column l16
+    float m_col = NEG_INF; // reference maximum of column l16 (log2 units)
+    int cur_item = -1, cur_s = 0, cur_g = 0;
+
+    auto reset = [&](int s, int g) __attribute__((always_inline)) {
+        const bool valid = l16 < G;
+        const char *qrow = (const char *)query +
+                           ((int64_t)s * num_q_heads + (int64_t)g * G + (valid ? l16 : 0)) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = *(const u32x4 *)(qrow + ks * 64 + lg * 16);
+            qt[ks] = valid ? v : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x4_mv{0.f, 0.f, 0.f, 0.f};
+        acc_l = f32x4_mv{0.f, 0.f, 0.f, 0.f};
+        m_col = NEG_INF;
+    };
+
+    // Write the finished pair: to out when this wave saw all of it, else as a
+    // partial record (the layout decode_stream_kernel writes).
+    auto finish = [&]() __attribute__((always_inline)) {
+        const int us = scan[cur_s + 1] - scan[cur_s];
+        const int64_t u0 = (int64_t)scan[cur_s] * Hkv + (int64_t)cur_g * us;
+        const bool whole = u0 >= ua && u0 + us <= ub;
+        const float lsum = __shfl(acc_l[0], l16);
+        if (l16 >= G) return;
+        const int64_t qrow = (int64_t)cur_s * num_q_heads + (int64_t)cur_g * G + l16;
+        if (whole) {
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                uint2 v;
+                v.x = pack_bf16x2(acc_o[dt][0] * inv, acc_o[dt][1] * inv);
+                v.y = pack_bf16x2(acc_o[dt][2] * inv, acc_o[dt][3] * inv);
+                *(uint2 *)(out + qrow * D + dt * 16 + lg * 4) = v;
+            }
+        } else {
+            const int64_t rid = (int64_t)(cur_item + gw) * G + l16;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *(float4 *)(rec_o + rid * D + dt * 16 + lg * 4) =
+                    make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+            if (lg == 0) *(float2 *)(rec_ml + rid * 2) = make_float2(m_col, lsum);
+        }
+    };
+
+    for (int64_t base = ua; base < ub; base += 64) {
+        const int n = (int)min((int64_t)64, ub - base);
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1;
+        int l_s = 0, l_j = 0, l_us = 1;
+        if (lane < n) {  // from the LDS scan alone
+            const int64_t u = base + lane;
+            l_s = seq_of_unit(scan, S, u, Hkv);
+            l_us = scan[l_s + 1] - scan[l_s];
+            const int rem = (int)(u - (int64_t)scan[l_s] * Hkv);
+            const int g = rem / l_us;
+            l_j = rem - g * l_us;
+            l_item = l_s * Hkv + g;
+        }
+        // Append (see decode_stream_kernel): the rows of the first PE pairs
+        // that end in this chunk are fetched with the descriptors.
+        constexpr int PE = 64 / (2 * NCH);
+        const int grp = lane / (2 * NCH), c2 = lane % (2 * NCH);
+        const bool c2v = c2 >= NCH;
+        const int c2ch = c2v ? c2 - NCH : c2;
+        uint64_t ends = 0;
+        int first = -1;
+        u32x4 first_row = {0, 0, 0, 0};
+        if (AP) {
+            ends = __builtin_amdgcn_ballot_w64(lane < n && l_j == l_us - 1);
+#pragma unroll
+            for (int e = 0; e < PE; ++e) {
+                if (ends) {
+                    const int bit = (int)__builtin_ctzll(ends);
+                    ends &= ends - 1;
+                    if (grp == e) first = bit;
+                }
+            }
+            const int it = __shfl(l_item, first < 0 ? 0 : first);
+            if (first >= 0)
+                first_row = *(const u32x4 *)((const char *)(c2v ? new_value : new_key) +
+                                             (int64_t)it * ROWB + c2ch * 16);
+        }
+        if (lane < n) {
+            const int Lraw = context_lens[l_s];
+            const int L = clamp_len(Lraw, max_tokens);
+            const int tok = l_j * kUnitTokens;
+            l_nvalid = min(kUnitTokens, L - tok);
+            l_tokoff = tok % B;
+            const int phys = block_tables[(int64_t)l_s * max_blocks + tok / B];
+            if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
+            l_phys = phys;
+            if (AP && Lraw == L && l_j == l_us - 1 && l_nvalid > 0) l_new = l_nvalid - 1;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
+        if (AP) {
+            auto put = [&](int mine, const u32x4 &row) __attribute__((always_inline)) {
+                const int src_lane = mine < 0 ? 0 : mine;
+                const int it = __shfl(l_item, src_lane), ph = __shfl(l_phys, src_lane);
+                const int to = __shfl(l_tokoff, src_lane), nr = __shfl(l_new, src_lane);
+                if (mine >= 0 && nr >= 0) {
+                    char *dst = (char *)(c2v ? value_cache : key_cache) + (int64_t)ph * block_bytes +
+                                (int64_t)(it % Hkv) * head_bytes + (int64_t)(to + nr) * ROWB +
+                                c2ch * 16;
+                    *(u32x4 *)dst = row;
+                }
+            };
+            put(first, first_row);
+            while (ends) {
+                int mine = -1;
+#pragma unroll
+                for (int e = 0; e < PE; ++e) {
+                    if (ends) {
+                        const int bit = (int)__builtin_ctzll(ends);
+                        ends &= ends - 1;
+                        if (grp == e) mine = bit;
+                    }
+                }
+                const int it = __shfl(l_item, mine < 0 ? 0 : mine);
+                u32x4 row = {0, 0, 0, 0};
+                if (mine >= 0)
+                    row = *(const u32x4 *)((const char *)(c2v ? new_value : new_key) +
+                                           (int64_t)it * ROWB + c2ch * 16);
+                put(mine, row);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+
+        // Issue unit i of the chunk into buffer b: V by DMA into the wave's
+        // slot b, then K into registers (waiting for K then also covers the
+        // older DMA).  Units past the segment get empty ranges: no memory is
+        // touched and zeros land.
+        u32x4 kb[NB][KS];
+        int nv[NB];
+        auto issue = [&](int b, int i, int seg_end) __attribute__((always_inline)) {
+            const int ii = i & 63;
+            const int nvalid = (i < seg_end) ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
+            const int item = __builtin_amdgcn_readlane(l_item, ii);
+            const int phys = __builtin_amdgcn_readlane(l_phys, ii);
+            const int tokoff = __builtin_amdgcn_readlane(l_tokoff, ii);
+            const int64_t off = nvalid > 0 ? (int64_t)phys * block_bytes +
+                                                 (int64_t)(item % Hkv) * head_bytes +
+                                                 (int64_t)tokoff * ROWB
+                                           : 0;
+            const int range = nvalid > 0 ? nvalid * ROWB : 0;
+            nv[b] = nvalid;
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, 0x00020000);
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const int row = sg * KPS + dma_row;
+                dma16_to_lds(rv, &vslot[w][b][sg * 1024],
+                             row * ROWB + ((dma_ch ^ mma_swz<D>(row)) << 4));
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kb[b][ks] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + ks * 64, 0, 0));
+        };
+
+        // One unit: logits, online softmax per column, P V.
+        auto process = [&](int b) __attribute__((always_inline)) {
+            f32x4_mv st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_mv, kb[b][ks]),
+                                                             __builtin_bit_cast(bf16x8_mv, qt[ks]),
+                                                             st, 0, 0, 0);
+            // V^T reads of the slot, in flight while the softmax runs.
+            const uint32_t vb = lds_offset(&vslot[w][b][0]) + v_lane;
+            s16x4_mv va[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_tr16(vb ^ ((uint32_t)dt << 5));
+            float x[4];
+            bool need = m_col == NEG_INF;
+            float lmax = NEG_INF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (4 * lg + i < nv[b]) ? st[i] * scale_log2 : NEG_INF;
+                lmax = fmaxf(lmax, x[i]);
+            }
+            need |= lmax > m_col + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = fmaxf(m_col, max4_lanes(lmax));
+                const float alpha = (m_col == NEG_INF) ? 0.f : fast_exp2(m_col - mn);
+                m_col = mn;
+                acc_l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+            }
+            const float mneg = (m_col == NEG_INF) ? 0.f : -m_col;
+            uint32_t p01 = pack_bf16x2(fast_exp2(x[0] + mneg), fast_exp2(x[1] + mneg));
+            uint32_t p23 = pack_bf16x2(fast_exp2(x[2] + mneg), fast_exp2(x[3] + mneg));
+            const s16x4_mv pt = __builtin_bit_cast(s16x4_mv, (uint64_t)p01 | ((uint64_t)p23 << 32));
+            acc_l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones_a, pt, acc_l, 0, 0, 0);
+            if constexpr (DT == 8) lds_tr_wait<8>(va); else lds_tr_wait<4>(va);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pt, acc_o[dt], 0, 0, 0);
+        };
+
+        for (int i0 = 0; i0 < n;) {
+            const int item = __builtin_amdgcn_readlane(l_item, i0);
+            const uint64_t other =
+                __builtin_amdgcn_ballot_w64(lane < n && lane > i0 && l_item != item);
+            const int i1 = other ? (int)__builtin_ctzll(other) : n;  // segment end
+            if (item != cur_item) {
+                if (cur_item >= 0) finish();
+                cur_item = item;
+                cur_s = item / Hkv;
+                cur_g = item - cur_s * Hkv;
+                reset(cur_s, cur_g);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) issue(b, i0 + b, i1);
+            for (int i = i0; i < i1; i += NB) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (nv[b] > 0) process(b);
+                    issue(b, i + NB + b, i1);
                 }
             }
             i0 = i1;
@@ -843,8 +1194,37 @@ static int max_tokens(const DecodeArgs &a) {
     return (int)m;
 }
 
+#ifndef PA_DECODE_MMA
+#define PA_DECODE_MMA 1
+#endif
+
+template <int D, int B, int G>
+static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid(cdiv(a.stream_waves, kMmaWaves));
+    const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
+    if (a.new_key)
+        hipLaunchKernelGGL((decode_stream_mma_kernel<D, B, G, kMmaWaves, true>), grid,
+                           dim3(kMmaWaves * 64), dyn, stream, (bf16_t *)a.out,
+                           (const bf16_t *)a.query, (bf16_t *)a.key_cache, (bf16_t *)a.value_cache,
+                           a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads,
+                           a.num_kv_heads, a.max_blocks_per_seq, max_tokens(a), a.num_blocks,
+                           a.stream_waves, a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
+                           (const bf16_t *)a.new_key, (const bf16_t *)a.new_value);
+    else
+        hipLaunchKernelGGL((decode_stream_mma_kernel<D, B, G, kMmaWaves, false>), grid,
+                           dim3(kMmaWaves * 64), dyn, stream, (bf16_t *)a.out,
+                           (const bf16_t *)a.query, (bf16_t *)a.key_cache, (bf16_t *)a.value_cache,
+                           a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads,
+                           a.num_kv_heads, a.max_blocks_per_seq, max_tokens(a), a.num_blocks,
+                           a.stream_waves, a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
+                           (const bf16_t *)nullptr, (const bf16_t *)nullptr);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int B, int G>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
+    if (PA_DECODE_MMA && std::is_same<T, bf16_t>::value && a.stream_waves > 0)
+        return launch_stream_mma<D, B, G>(a, stream);
     if (a.stream_waves > 0) {
         dim3 grid(cdiv(a.stream_waves, kDecodeWaves));
         if (a.new_key)
