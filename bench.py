@@ -64,6 +64,7 @@ def parse():
 # Sources each kernel is built from; the traffic figures in
 # profiles/hbm_traffic.txt are only reported while these are unchanged.
 KERNEL_SOURCES = {
+    "decode_stream_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
@@ -249,8 +250,9 @@ def main():
     t_pf = avg_ms("pf0", "pf1") if chunks else 0.0
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    dp_kernel = ("decode_stream_kernel"
-                 if P == 0 and S <= 8192 else "decode_partition_kernel")
+    # bf16 uses the matrix-core variant of the balanced split.
+    dp_kernel = ("decode_partition_kernel" if P != 0 or S > 8192 else
+                 "decode_stream_mma_kernel" if case.dtype == "bf16" else "decode_stream_kernel")
     # The fused step's decode kernel also moves the new tokens' rows.
     dp_bytes = dec_bytes + (cw_bytes if fused else 0)
     dp_gbs = dp_bytes / (t_dp * 1e-3) / 1e9

@@ -621,7 +621,10 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
 // work split, records and reduce are those of decode_stream_kernel.
 // ---------------------------------------------------------------------------
 
-constexpr int kMmaBuffers = 3;  // units in flight + 1 per wave
+#ifndef PA_MMA_BUFFERS
+#define PA_MMA_BUFFERS 3
+#endif
+constexpr int kMmaBuffers = PA_MMA_BUFFERS;  // units in flight + 1 per wave
 constexpr int kMmaWaves = 4;    // waves per workgroup
 
 typedef __bf16 bf16x8_mv __attribute__((ext_vector_type(8)));
