@@ -969,6 +969,11 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
     typedef float vecd __attribute__((ext_vector_type(DPL)));
     float2 w0 = make_float2(NEG_INF, 0.f);
     if (lane < nrec) w0 = *(const float2 *)(ml + lane * ml_stride);
+    // The outputs of the first 8 records go out with the weights (they do not
+    // depend on them), so a row of up to 8 records costs one round trip.
+    vecd v0[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v0[j] = *(const vecd *)(o + min(j, nrec - 1) * o_stride + lane * DPL);
     float M = w0.x;
     for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, ml[k * ml_stride]);
     M = wave_max(M);
@@ -988,7 +993,7 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int k = c0 + min(j0 + j, n - 1);  // padded slots reload a valid record
-                v[j] = *(const vecd *)(o + k * o_stride + lane * DPL);
+                v[j] = (c0 == 0 && j0 == 0) ? v0[j] : *(const vecd *)(o + k * o_stride + lane * DPL);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {

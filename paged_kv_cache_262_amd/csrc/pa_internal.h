@@ -28,9 +28,15 @@ hipError_t launch_append_rows(const void *key, const void *value, void *key_cach
 // scan the per-sequence unit counts in LDS.  Larger batches use fixed
 // partitions.
 constexpr int kStreamMaxSeqs = 8192;
-// Waves the balanced split spreads the work over (256 CUs x 8 resident waves
-// on MI355X); a constant, so results do not depend on the device.
-constexpr int kStreamWaves = 2048;
+// Waves the balanced split spreads the work over: one per SIMD of MI355X's
+// 256 CUs.  With two waves per SIMD the older one wins most of the memory
+// issue slots and the younger one finishes far later, so the kernel ends on a
+// long tail; one wave per SIMD with the same loads in flight ends sooner.  A
+// constant, so results do not depend on the device.
+#ifndef PA_STREAM_WAVES
+#define PA_STREAM_WAVES 1024
+#endif
+constexpr int kStreamWaves = PA_STREAM_WAVES;
 
 struct DecodeArgs {
     void *out;

@@ -54,9 +54,10 @@ def test_auto_partition_and_workspace(lib):
     np_ = -(-4096 // 512)
     need = lib.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 512)
     assert need >= 64 * 32 * np_ * (128 + 2) * 4
-    # balanced split: one record per (seq, kv head) plus one per wave, G heads each
+    # balanced split: one record per (seq, kv head) plus one per wave (1024 waves),
+    # G heads each, and the unit scan
     need = lib.pa_decode_workspace_bytes(64, 32, 8, 128, 16, 4096, 0)
-    assert need >= (64 * 8 + 2048) * 4 * (128 + 2) * 4 + 65 * 4
+    assert need >= (64 * 8 + 1024) * 4 * (128 + 2) * 4 + 65 * 4
     # one partition needs no real workspace
     assert lib.pa_decode_workspace_bytes(4, 4, 4, 64, 16, 100, 128) == 256
 
