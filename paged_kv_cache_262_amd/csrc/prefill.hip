@@ -122,7 +122,7 @@ struct KvLds {
     static constexpr int STAGE_BYTES = 4 * BLOCK_BYTES;   // K even, K odd, V even, V odd
     static constexpr int SEGS_PER_WAVE = 4 * SEGS / kPfWaves;
     static_assert(4 * SEGS % kPfWaves == 0, "segments split evenly over the waves");
-    static __device__ __forceinline__ int swz(int key) {
+    static __host__ __device__ constexpr int swz(int key) {
         return D == 128 ? (key & 7) << 1 : ((key >> 1) & 3) << 1;
     }
 };
@@ -229,25 +229,39 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     // ---- DMA of one pair of key blocks into a stage -------------------------
     // The stage's 4 * SEGS segments of 1 KB ([K even][K odd][V even][V odd])
     // are split over the waves; lane i of a segment moves chunk i % NCH of row
-    // i / NCH.  The rows of a segment lie in one page, so the page lookup and
-    // the page address are wave-uniform (scalar).  In the tile's last block,
+    // i / NCH.  The rows of a segment lie in one page, so each segment is one
+    // global_load_lds from a wave-uniform page address plus a per-lane offset
+    // that depends only on the segment's parity.  In the tile's last block,
     // keys past kend read the row of key kend - 1 instead (data whose weight
     // is exactly 0), so no LDS row is ever left stale.
     const int seg_row = lane / LY::NCH, seg_ch = lane % LY::NCH;
     static_assert(B % LY::KPS == 0, "a segment's rows share a page");
     static_assert(LY::SEGS_PER_WAVE <= 64, "one lane per segment");
-    // Lane j < SEGS_PER_WAVE looks up the page of the wave's segment j of pair
-    // pr, so all lookups of a pair cost one LDS round trip.
-    auto lookup_pages = [&](int pr) __attribute__((always_inline)) {
+    static_assert(LY::swz(2 * LY::KPS) == LY::swz(0) && LY::swz(3 * LY::KPS) == LY::swz(LY::KPS),
+                  "the chunk permutation of a segment depends on its parity only");
+    uint32_t seg_lane_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        seg_lane_off[par] = (uint32_t)(seg_row * ROWB +
+                                       ((seg_ch ^ LY::swz(par * LY::KPS + seg_row)) << 4));
+    // Lane j < SEGS_PER_WAVE computes the global address of the first row of
+    // the wave's segment j of pair pr (its page looked up in the window,
+    // out-of-range entries replaced by block 0), all segments in one pass.
+    auto lookup_pages = [&](int pr) __attribute__((always_inline)) -> uint64_t {
         const int j = lane < LY::SEGS_PER_WAVE ? lane : 0;
         const int seg = w * LY::SEGS_PER_WAVE + j;
-        const int kb = 2 * pr + ((seg / LY::SEGS) & 1);
+        const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1;
+        const int kb = 2 * pr + bp;
         const int key_s = min(kb * kKeyBlock + (seg % LY::SEGS) * LY::KPS, kend - 1);
-        return bt_s[key_s / B - win_p0];
+        int phys = bt_s[key_s / B - win_p0];
+        if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;  // caller error: block 0
+        const char *pool = (const char *)(tensor ? value_cache : key_cache);
+        return (uint64_t)(uintptr_t)(pool + ((int64_t)phys * block_elems + (int64_t)g * B * D) * 2 +
+                                     (key_s % B) * ROWB);
     };
-    // This wave's share of the DMA of pair pr into stage (seg_phys from
+    // This wave's share of the DMA of pair pr into stage (seg_addr from
     // lookup_pages(pr)).
-    auto issue_dma = [&](char *stage, int pr, int seg_phys) __attribute__((always_inline)) {
+    auto issue_dma = [&](char *stage, int pr, uint64_t seg_addr) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < LY::SEGS_PER_WAVE; ++j) {
             const int seg = w * LY::SEGS_PER_WAVE + j;  // uniform
@@ -255,23 +269,22 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
             const int s = seg % LY::SEGS;
             const int kb = 2 * pr + bp;
             if (kb >= nkb) continue;  // block past the tile's keys
-            const char *pool = (const char *)(tensor ? value_cache : key_cache);
             lds_void *dst = (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024);
-            const int kk = s * LY::KPS + seg_row;
-            const int chunk_off = (seg_ch ^ LY::swz(kk)) << 4;
-            const int key_s = kb * kKeyBlock + s * LY::KPS;  // the segment's first key
             if (kb * kKeyBlock + kKeyBlock <= kend) {
-                int phys = __builtin_amdgcn_readlane(seg_phys, j);
-                if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;  // caller error: block 0
-                const char *page = pool + ((int64_t)phys * block_elems + (int64_t)g * B * D) * 2;
-                const uint32_t off = (uint32_t)((key_s % B + seg_row) * ROWB + chunk_off);
-                __builtin_amdgcn_global_load_lds((const void *)(page + off), dst, 16, 0, 0);
+                const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)seg_addr, j);
+                const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(seg_addr >> 32), j);
+                const char *page = (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+                __builtin_amdgcn_global_load_lds((const void *)(page + seg_lane_off[s & 1]), dst, 16,
+                                                 0, 0);
             } else {
-                const int key = min(key_s + seg_row, kend - 1);
+                const int kk = s * LY::KPS + seg_row;
+                const int key = min(kb * kKeyBlock + kk, kend - 1);
                 int phys = bt_s[key / B - win_p0];
                 if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;
+                const char *pool = (const char *)(tensor ? value_cache : key_cache);
                 const char *src = pool + ((int64_t)phys * block_elems +
-                                          ((int64_t)g * B + key % B) * D) * 2 + chunk_off;
+                                          ((int64_t)g * B + key % B) * D) * 2 +
+                                  ((seg_ch ^ LY::swz(kk)) << 4);
                 __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
             }
         }
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     // dma_stage != nullptr: issue this wave's share of the DMA of pair
     // dma_pair after the softmax, before the P V products.
     auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
-                       int seg_phys) __attribute__((always_inline)) {
+                       uint64_t seg_phys) __attribute__((always_inline)) {
         floatx4_v s[4][RT];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -404,7 +417,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
         __syncthreads();  // cur's DMA landed (every wave waited for its own); nxt is free
         const bool next = pr + 1 < npairs;
-        int seg_phys = 0;
+        uint64_t seg_phys = 0;
         if (next) {
             if (2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
                 load_window(2 * (pr + 1));
