@@ -25,7 +25,8 @@ _lib = None
 
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 STATUS = {0: "ok", 1: "invalid argument", 2: "block id out of range",
-          3: "slot out of range", 4: "duplicate slot", 5: "out of memory"}
+          3: "slot out of range", 4: "duplicate slot or destination block", 5: "out of memory",
+          6: "block both source and destination of an in-place copy"}
 
 
 class OracleError(RuntimeError):
@@ -51,8 +52,9 @@ def load(path: str | None = None):
     lib.oracle_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                    i64, ctypes.c_float, i32]
     lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32]
+    lib.oracle_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32]
     for f in (lib.oracle_gather, lib.oracle_decode, lib.oracle_prefill,
-              lib.oracle_reshape_and_cache):
+              lib.oracle_reshape_and_cache, lib.oracle_copy_blocks):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -131,3 +133,22 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, lib=None
     _check(lib.oracle_reshape_and_cache(_ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(slots), T,
                                         Hkv, D, B, NB, key.element_size()))
     return kc, vc
+
+
+def copy_blocks(src_key, src_value, dst_key, dst_value, block_mapping, lib=None):
+    """Copy whole blocks src -> dst (pairs of block ids, [n, 2] int64), K and V.
+
+    Returns new destination pools (copies of dst_* with the blocks written).
+    Passing the same tensors as source and destination is the in-place case
+    (copy-on-write inside one pool)."""
+    lib = lib or load()
+    in_place = src_key is dst_key
+    assert (src_value is dst_value) == in_place
+    sk, sv = src_key.contiguous(), src_value.contiguous()
+    dk, dv = dst_key.clone().contiguous(), dst_value.clone().contiguous()
+    assert sk.shape[1:] == dk.shape[1:] and sk.dtype == dk.dtype
+    m = torch.as_tensor(block_mapping, dtype=torch.int64).reshape(-1, 2).contiguous()
+    block_bytes = sk[0].numel() * sk.element_size() if sk.shape[0] else dk[0].numel() * dk.element_size()
+    _check(lib.oracle_copy_blocks(_ptr(sk), _ptr(sv), _ptr(dk), _ptr(dv), _ptr(m), m.shape[0],
+                                  sk.shape[0], dk.shape[0], block_bytes, int(in_place)))
+    return dk, dv

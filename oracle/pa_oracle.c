@@ -301,3 +301,77 @@ int oracle_reshape_and_cache(const void *key, const void *value, void *key_cache
     }
     return 0;
 }
+
+/* ---- block copy: copy-on-write and swap --------------------------------- */
+
+/*
+ * Blocks that several sequences share are copied before one of them writes
+ * into its own copy ("vLLM Guide: High-Throughput Multi-GPU LLM Serving with
+ * PagedAttention", section "What Is PagedAttention?": shared physical blocks
+ * with copy-on-write), and under memory pressure the pages of a paused
+ * request move to host memory and later back ("Configuring vLLM and
+ * PagedAttention for High Throughput Enterprise LLM Serving", section "Quick
+ * Answers", the question on KV-cache offloading when VRAM is full).
+ *
+ * For every pair i, block mapping[2i] of the source pools is copied bit for
+ * bit (block_bytes per pool: all kv heads, block_size rows, head_dim) into
+ * block mapping[2i + 1] of the destination pools, K and V alike.  Every read
+ * happens before any write (the sources are snapshotted).  Errors, with
+ * nothing written: a block id outside its pool (2), a destination named twice
+ * (4), and, when source and destination are the same pools (in_place), a
+ * block that is both a source and a destination (6).
+ */
+int oracle_copy_blocks(const void *src_key, const void *src_value, void *dst_key,
+                       void *dst_value, const int64_t *mapping, int num_pairs,
+                       int64_t src_num_blocks, int64_t dst_num_blocks, int64_t block_bytes,
+                       int in_place)
+{
+    if (num_pairs < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+        return 1;
+    if (num_pairs == 0)
+        return 0;
+    unsigned char *is_dst = calloc((size_t)(dst_num_blocks > 0 ? dst_num_blocks : 1), 1);
+    if (!is_dst)
+        return 5;
+    for (int i = 0; i < num_pairs; ++i) {
+        int64_t s = mapping[2 * i], d = mapping[2 * i + 1];
+        if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks) {
+            free(is_dst);
+            return 2;
+        }
+        if (is_dst[d]) {
+            free(is_dst);
+            return 4;
+        }
+        is_dst[d] = 1;
+    }
+    if (in_place) {
+        for (int i = 0; i < num_pairs; ++i) {
+            if (is_dst[mapping[2 * i]]) {
+                free(is_dst);
+                return 6;
+            }
+        }
+    }
+    free(is_dst);
+    size_t snap_bytes = (size_t)num_pairs * (size_t)block_bytes;
+    char *snap_k = malloc(snap_bytes), *snap_v = malloc(snap_bytes);
+    if (!snap_k || !snap_v) {
+        free(snap_k);
+        free(snap_v);
+        return 5;
+    }
+    for (int i = 0; i < num_pairs; ++i) {
+        size_t src = (size_t)mapping[2 * i] * (size_t)block_bytes;
+        memcpy(snap_k + (size_t)i * block_bytes, (const char *)src_key + src, (size_t)block_bytes);
+        memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_value + src, (size_t)block_bytes);
+    }
+    for (int i = 0; i < num_pairs; ++i) {
+        size_t dst = (size_t)mapping[2 * i + 1] * (size_t)block_bytes;
+        memcpy((char *)dst_key + dst, snap_k + (size_t)i * block_bytes, (size_t)block_bytes);
+        memcpy((char *)dst_value + dst, snap_v + (size_t)i * block_bytes, (size_t)block_bytes);
+    }
+    free(snap_k);
+    free(snap_v);
+    return 0;
+}

@@ -11,7 +11,9 @@ raises AssertionError when the oracle disagrees with:
     mean of V; a dominant key returns its V),
   * invariants (relabelling physical blocks; shared vs private prefix blocks;
     softmax rows summing to one),
-  * the cache-write contract (slots hit, everything else untouched, bitwise).
+  * the cache-write contract (slots hit, everything else untouched, bitwise),
+  * the block-copy contract (coded blocks land whole; copy-on-write and a swap
+    round trip with the table redirected leave attention unchanged).
 """
 from __future__ import annotations
 
@@ -359,6 +361,104 @@ def pin_cache_write_rejects_bad_slots(lib):
         assert e.code == 4
 
 
+# -------------------------------------------------------------- block copy --
+
+def _used_blocks(c):
+    used = set()
+    for s in range(c.num_seqs):
+        nb = -(-int(c.context_lens[s]) // c.block_size)
+        used.update(int(x) for x in c.block_tables[s, :nb].tolist())
+    return used
+
+
+def pin_copy_blocks_moves_whole_blocks(lib):
+    """On coded pools (every element names its block, offset and head), each
+    destination block afterwards holds exactly its source block's codes, in K
+    and V alike, and every other destination block is unchanged: across pools
+    (swap) and inside one pool (copy-on-write)."""
+    NB, Hkv, B, D = 12, 2, 16, 64
+    kc = _coded_pool(NB, Hkv, B, D)
+    vc = kc * 2.0 + 1.0
+    # across pools: a smaller destination pool, one source copied twice
+    dk0 = torch.full((6, Hkv, B, D), -7.0)
+    dv0 = dk0.clone()
+    pairs = [(3, 5), (0, 1), (11, 0), (3, 2)]
+    dk, dv = oracle.copy_blocks(kc, vc, dk0, dv0, pairs, lib=lib)
+    offs = torch.arange(B, dtype=torch.float32)[None, :]
+    heads = torch.arange(Hkv, dtype=torch.float32)[:, None]
+    for src, dst in pairs:
+        assert torch.all(dk[dst, :, :, 0] == src) and torch.all(dk[dst, :, :, 1] == offs)
+        assert torch.all(dk[dst, :, :, 2] == heads) and torch.all(dk[dst, :, :, 3] == 1.0)
+        assert torch.all(dv[dst, :, :, 0] == 2 * src + 1)
+    for d in (3, 4):
+        assert torch.all(dk[d] == -7.0) and torch.all(dv[d] == -7.0)
+    # inside one pool
+    k2, v2 = oracle.copy_blocks(kc, vc, kc, vc, [(1, 9), (4, 10)], lib=lib)
+    for src, dst in ((1, 9), (4, 10)):
+        assert torch.all(k2[dst, :, :, 0] == src) and torch.all(v2[dst, :, :, 0] == 2 * src + 1)
+    for b in set(range(NB)) - {9, 10}:
+        assert torch.equal(k2[b], kc[b]) and torch.equal(v2[b], vc[b])
+
+
+def pin_copy_on_write_keeps_attention(lib):
+    """Copying a sequence's blocks to free blocks and pointing its table at the
+    copies (copy-on-write before a write) leaves every decode output bit for
+    bit unchanged."""
+    for dtype in ("f32", "bf16"):
+        c = W.random_case(61, dtype, 3, 8, 2, 64, 16, 20, 90, write_new=False, extra_blocks=8)
+        ref = oracle.decode(c.query, c.key_cache, c.value_cache, c.block_tables,
+                            c.context_lens, c.scale, lib=lib)
+        free = sorted(set(range(c.key_cache.shape[0])) - _used_blocks(c))
+        nb0 = -(-int(c.context_lens[0]) // c.block_size)
+        assert len(free) >= nb0
+        pairs = [(int(c.block_tables[0, j]), free[j]) for j in range(nb0)]
+        kc, vc = oracle.copy_blocks(c.key_cache, c.value_cache, c.key_cache, c.value_cache,
+                                    pairs, lib=lib)
+        bt = c.block_tables.clone()
+        bt[0, :nb0] = torch.tensor([d for _, d in pairs], dtype=torch.int32)
+        out = oracle.decode(c.query, kc, vc, bt, c.context_lens, c.scale, lib=lib)
+        assert np.array_equal(ref, out)
+
+
+def pin_swap_round_trip(lib):
+    """Swapping a sequence's blocks out to a host pool and back into other
+    free blocks (table redirected) gives the same decode output bit for bit;
+    the host pool holds the blocks in swap order."""
+    c = W.random_case(67, "bf16", 3, 8, 2, 128, 16, 30, 100, write_new=False, extra_blocks=8)
+    ref = oracle.decode(c.query, c.key_cache, c.value_cache, c.block_tables, c.context_lens,
+                        c.scale, lib=lib)
+    nb1 = -(-int(c.context_lens[1]) // c.block_size)
+    own = [int(x) for x in c.block_tables[1, :nb1].tolist()]
+    hk0 = torch.zeros((nb1,) + tuple(c.key_cache.shape[1:]), dtype=c.key_cache.dtype)
+    hk, hv = oracle.copy_blocks(c.key_cache, c.value_cache, hk0, hk0.clone(),
+                                [(b, i) for i, b in enumerate(own)], lib=lib)
+    for i, b in enumerate(own):
+        assert torch.equal(hk[i].view(torch.int16), c.key_cache[b].view(torch.int16))
+        assert torch.equal(hv[i].view(torch.int16), c.value_cache[b].view(torch.int16))
+    free = sorted(set(range(c.key_cache.shape[0])) - _used_blocks(c))[:nb1]
+    kc, vc = oracle.copy_blocks(hk, hv, c.key_cache, c.value_cache,
+                                [(i, f) for i, f in enumerate(free)], lib=lib)
+    bt = c.block_tables.clone()
+    bt[1, :nb1] = torch.tensor(free, dtype=torch.int32)
+    out = oracle.decode(c.query, kc, vc, bt, c.context_lens, c.scale, lib=lib)
+    assert np.array_equal(ref, out)
+
+
+def pin_copy_blocks_rejects(lib):
+    kc = _coded_pool(6, 1, 16, 64)
+    vc = kc.clone()
+    k, v = oracle.copy_blocks(kc, vc, kc, vc, torch.zeros((0, 2), dtype=torch.int64), lib=lib)
+    assert torch.equal(k, kc) and torch.equal(v, vc)
+    for pairs, code, same in (([(0, 6)], 2, True), ([(-1, 2)], 2, True), ([(0, 2), (1, 2)], 4, True),
+                              ([(0, 2), (2, 3)], 6, True), ([(0, 2), (2, 3)], 0, False)):
+        dk, dv = (kc, vc) if same else (kc.clone(), vc.clone())
+        try:
+            oracle.copy_blocks(kc, vc, dk, dv, pairs, lib=lib)
+            assert code == 0, f"{pairs} accepted"
+        except oracle.OracleError as e:
+            assert e.code == code, (pairs, e.code)
+
+
 ALL_PINS = [
     pin_gather_page_examples,
     pin_decode_one_hot_page_examples,
@@ -376,4 +476,8 @@ ALL_PINS = [
     pin_prefill_last_row_is_decode,
     pin_cache_write,
     pin_cache_write_rejects_bad_slots,
+    pin_copy_blocks_moves_whole_blocks,
+    pin_copy_on_write_keeps_attention,
+    pin_swap_round_trip,
+    pin_copy_blocks_rejects,
 ]

@@ -54,6 +54,13 @@ MUTATIONS = {
                        "memcpy((char *)value_cache + dst, (const char *)key + src, row_bytes);"),
     "write_keeps_duplicates": ("if (seen[s]) {", "if (0) {"),
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
+    "copy_v_from_k": ("memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_value + src,",
+                      "memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_key + src,"),
+    "copy_wrong_source": ("size_t src = (size_t)mapping[2 * i] * (size_t)block_bytes;",
+                          "size_t src = (size_t)mapping[2 * i + 1] * (size_t)block_bytes;"),
+    "copy_keeps_duplicates": ("if (is_dst[d]) {", "if (0) {"),
+    "copy_half_block": ("memcpy((char *)dst_key + dst, snap_k + (size_t)i * block_bytes, (size_t)block_bytes);",
+                        "memcpy((char *)dst_key + dst, snap_k + (size_t)i * block_bytes, (size_t)block_bytes / 2);"),
     "q_from_wrong_head": ("q[i] = widen(q_base, q_off + i, dtype);",
                           "q[i] = widen(q_base, (q_off / D / 2) * D * 2 + i, dtype);"),
 }
