@@ -243,6 +243,44 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                            int32_t dtype, void *stream);
 
+/*
+ * pa_copy_blocks -- copy whole KV blocks between pools: copy-on-write inside
+ * the device pool, and swap of a paused request's pages to host memory and
+ * back.
+ *
+ * Shared physical blocks are copied before one sequence writes into its own
+ * copy ("vLLM Guide: High-Throughput Multi-GPU LLM Serving with
+ * PagedAttention", section "What Is PagedAttention?": copy-on-write), and when
+ * the pool is full the pages of a paused request move to host RAM over PCIe
+ * and later back ("Configuring vLLM and PagedAttention for High Throughput
+ * Enterprise LLM Serving", section "Quick Answers", the question on KV-cache
+ * offloading).
+ *
+ * For every pair i < num_pairs, block block_mapping[2i] of the source pools
+ * is copied bit for bit into block block_mapping[2i + 1] of the destination
+ * pools, in the K pool and in the V pool.  A block is block_bytes bytes
+ * (num_kv_heads * block_size * head_dim * element bytes for the pool layout
+ * above; a multiple of 16).  Source and destination pools are
+ * [src_num_blocks] / [dst_num_blocks] blocks; they may be the same pools
+ * (copy-on-write).
+ *
+ * Memory: every pointer (the four pools and the int64 [num_pairs][2] mapping)
+ * must be device memory or pinned host memory that the device can map
+ * (hipHostMalloc); anything else is rejected with PA_ERR_INVALID_ARG before
+ * any launch.  The caller owns all of it.  Host pools are read or written by
+ * the kernel across PCIe; enqueue on the caller's stream, synchronise before
+ * touching host pools from the CPU.
+ *
+ * Preconditions (not checked: the mapping is device data): destination ids
+ * are distinct, and, for copies inside one pool, no block is both a source
+ * and a destination; otherwise the result depends on the order of the copies.
+ * Pairs with an id outside its pool are skipped.  num_pairs == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,
+                         void *dst_key_cache, void *dst_value_cache,
+                         const int64_t *block_mapping, int32_t num_pairs, int64_t src_num_blocks,
+                         int64_t dst_num_blocks, int64_t block_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,7 @@ library is missing every entry point raises.
 """
 from .binding import (  # noqa: F401
     PAError,
+    copy_blocks,
     decode,
     decode_append,
     decode_append_partitions,

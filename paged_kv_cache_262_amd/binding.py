@@ -45,6 +45,7 @@ SIGNATURES = {
                                            _vp, _sz, _vp]),
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
 }
 
 
@@ -233,3 +234,26 @@ def prefill_chunk(out, query, key_cache, value_cache, block_tables, cu_query_len
         int(max_query_len), Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
         _dtype(query), _stream(stream)))
     return out
+
+
+def copy_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, block_mapping,
+                stream=None):
+    """Copy whole blocks between pools: block_mapping [n, 2] int64 (source id,
+    destination id).  Pools are [NB, Hkv, B, D] tensors on the GPU or in pinned
+    host memory (pin_memory=True); the mapping likewise."""
+    for t, name in ((src_key_cache, "src_key_cache"), (src_value_cache, "src_value_cache"),
+                    (dst_key_cache, "dst_key_cache"), (dst_value_cache, "dst_value_cache"),
+                    (block_mapping, "block_mapping")):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int64 [n, 2]")
+    if src_key_cache.shape[1:] != dst_key_cache.shape[1:] or src_key_cache.dtype != dst_key_cache.dtype:
+        raise ValueError("source and destination pools differ in block shape or dtype")
+    block_bytes = src_key_cache[0].numel() * src_key_cache.element_size()
+    _check(load().pa_copy_blocks(
+        src_key_cache.data_ptr(), src_value_cache.data_ptr(), dst_key_cache.data_ptr(),
+        dst_value_cache.data_ptr(), block_mapping.data_ptr(), block_mapping.shape[0],
+        src_key_cache.shape[0], dst_key_cache.shape[0], block_bytes, _stream(stream)))

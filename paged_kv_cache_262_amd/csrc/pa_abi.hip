@@ -182,6 +182,28 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
     return PA_OK;
 }
 
+// The device address of p when the device can access it: device memory
+// (itself) or pinned host memory (its mapped view).  Pageable host memory, or
+// a pointer HIP does not know, gives false.  hipPointerGetAttributes is a
+// host-side query; its error, if any, is cleared so that it does not surface
+// at a later call.
+bool device_view(const void *p, const void **dev) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+        *dev = p;
+        return true;
+    }
+    if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer) {
+        *dev = (const char *)a.devicePointer + ((const char *)p - (const char *)a.hostPointer);
+        return true;
+    }
+    return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +412,38 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
     a.num_blocks = num_blocks;
     a.scale = scale;
     return hip_status(pa::launch_prefill_chunk(a, (hipStream_t)stream), "prefill_chunk");
+}
+
+pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,
+                         void *dst_key_cache, void *dst_value_cache,
+                         const int64_t *block_mapping, int32_t num_pairs, int64_t src_num_blocks,
+                         int64_t dst_num_blocks, int64_t block_bytes, void *stream) {
+    if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs < 0");
+    if (src_num_blocks < 0 || dst_num_blocks < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative pool size");
+    if (block_bytes <= 0 || block_bytes % 16)
+        return fail(PA_ERR_INVALID_ARG, "block_bytes %lld is not a positive multiple of 16",
+                    (long long)block_bytes);
+    if (num_pairs == 0) return PA_OK;
+    CHECK_PTR(src_key_cache, 16);
+    CHECK_PTR(src_value_cache, 16);
+    CHECK_PTR(dst_key_cache, 16);
+    CHECK_PTR(dst_value_cache, 16);
+    CHECK_PTR(block_mapping, 8);
+    const void *ptrs[5] = {src_key_cache, src_value_cache, dst_key_cache, dst_value_cache,
+                           block_mapping};
+    const char *names[5] = {"src_key_cache", "src_value_cache", "dst_key_cache",
+                            "dst_value_cache", "block_mapping"};
+    const void *dev[5];
+    for (int i = 0; i < 5; ++i)
+        if (!device_view(ptrs[i], &dev[i]))
+            return fail(PA_ERR_INVALID_ARG,
+                        "%s is neither device memory nor pinned host memory the device can map",
+                        names[i]);
+    return hip_status(pa::launch_copy_blocks(dev[0], dev[1], (void *)dev[2], (void *)dev[3],
+                                             (const int64_t *)dev[4], num_pairs, src_num_blocks,
+                                             dst_num_blocks, block_bytes, (hipStream_t)stream),
+                      "copy_blocks");
 }
 
 }  // extern "C"

@@ -60,6 +60,15 @@ struct DecodeArgs {
     const void *new_key, *new_value;
 };
 
+// Copies block mapping[2i] of the source pools to block mapping[2i + 1] of the
+// destination pools (block_bytes each, K and V); pairs with an id outside its
+// pool are skipped.  The pointers are device addresses (device memory, or
+// the device view of pinned host memory).
+hipError_t launch_copy_blocks(const void *src_key, const void *src_value, void *dst_key,
+                              void *dst_value, const int64_t *mapping, int num_pairs,
+                              int64_t src_num_blocks, int64_t dst_num_blocks, int64_t block_bytes,
+                              hipStream_t stream);
+
 // Returns hipErrorNotSupported when no kernel is built for the shape.
 hipError_t launch_decode_partitions(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream);
