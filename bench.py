@@ -58,6 +58,12 @@ def parse():
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--op", default="attention",
+                    choices=["attention", "copy_on_write", "swap_out", "swap_in"],
+                    help="attention: the hot-path step (default); the others time "
+                         "pa_copy_blocks on the workload's pool")
+    ap.add_argument("--copy-seqs", type=int, default=8,
+                    help="sequences whose blocks a copy op moves")
     return ap.parse_args()
 
 
@@ -144,6 +150,8 @@ def main():
     binding.load()
     dev = torch.device("cuda:0")
     case = W.NAMED[args.workload]()
+    if args.op != "attention":
+        return run_copy(args, case, dev)
     S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
                         case.block_size)
     eb = case.key_cache.element_size()
@@ -310,6 +318,100 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, kv_bytes)
+    print(json.dumps(result), flush=True)
+
+
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction: the host link of the swap
+
+
+def run_copy(args, case, dev):
+    """pa_copy_blocks on the workload's pool: the blocks of the first
+    --copy-seqs sequences are copied to fresh blocks of the same device pool
+    (copy_on_write), to a pinned host pool (swap_out) or from it back into
+    fresh device blocks (swap_in).  One launch per step."""
+    B = case.block_size
+    nbs = [-(-int(L) // B) for L in case.context_lens.tolist()[:args.copy_seqs]]
+    src = torch.cat([case.block_tables[s, :n] for s, n in enumerate(nbs)]).to(torch.int64)
+    n = src.numel()
+    NB = case.key_cache.shape[0]
+    kc = torch.cat([case.key_cache, torch.zeros_like(case.key_cache[:n])]).to(dev)
+    vc = torch.cat([case.value_cache, torch.zeros_like(case.value_cache[:n])]).to(dev)
+    fresh = torch.arange(NB, NB + n, dtype=torch.int64)
+    block_bytes = case.key_cache[0].numel() * case.key_cache.element_size()
+    if args.op == "copy_on_write":
+        sk, sv, dk, dv = kc, vc, kc, vc
+        mapping = torch.stack([src, fresh], 1)
+    else:
+        hk = torch.zeros((n,) + tuple(case.key_cache.shape[1:]), dtype=case.key_cache.dtype,
+                         pin_memory=True)
+        hv = torch.zeros_like(hk).pin_memory()
+        slots = torch.arange(n, dtype=torch.int64)
+        if args.op == "swap_out":
+            sk, sv, dk, dv = kc, vc, hk, hv
+            mapping = torch.stack([src, slots], 1)
+        else:
+            binding.copy_blocks(kc, vc, hk, hv, torch.stack([src, slots], 1).contiguous().to(dev))
+            sk, sv, dk, dv = hk, hv, kc, vc
+            mapping = torch.stack([slots, fresh], 1)
+    mapping = mapping.contiguous().to(dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        binding.copy_blocks(sk, sv, dk, dv, mapping, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+    for _ in range(args.steps):
+        binding.copy_blocks(sk, sv, dk, dv, mapping, stream=stream)
+    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    moved = 2 * n * block_bytes  # K and V blocks, each read once and written once
+    gbs = moved / (ms * 1e-3) / 1e9
+    if args.op == "copy_on_write":
+        roof = {"bound": "hbm", "achieved": round(2 * gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(2 * gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": 2 * moved, "kernel": "copy_blocks_kernel"}
+        ref = None
+    else:
+        roof = {"bound": "pcie", "achieved": round(gbs, 1), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": moved, "kernel": "copy_blocks_kernel"}
+        # the copy engine on one contiguous buffer of the same size, for reference
+        a = torch.empty(moved // 2, dtype=torch.uint8, device=dev)
+        h = torch.empty(moved // 2, dtype=torch.uint8, pin_memory=True)
+        for _ in range(3):
+            (h.copy_(a, non_blocking=True) if args.op == "swap_out" else a.copy_(h, non_blocking=True))
+        torch.cuda.synchronize()
+        f0 = torch.cuda.Event(enable_timing=True); f0.record(stream)
+        for _ in range(20):
+            (h.copy_(a, non_blocking=True) if args.op == "swap_out" else a.copy_(h, non_blocking=True))
+        f1 = torch.cuda.Event(enable_timing=True); f1.record(stream)
+        torch.cuda.synchronize()
+        ref = round(moved / 2 / (f0.elapsed_time(f1) / 20 * 1e-3) / 1e9, 1)
+    result = {
+        "metric": f"pa_copy_blocks {args.op} GB/s", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.op} of {args.copy_seqs} {case.name} sequences",
+                   "blocks": n, "block_bytes": block_bytes, "bytes_moved": moved},
+        "roofline": roof,
+    }
+    if ref is not None:
+        result["contiguous_copy_engine_GBs"] = ref
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = (case.key_cache, case.value_cache)
+        m = torch.stack([src, torch.arange(n, dtype=torch.int64)], 1)
+        dst = torch.zeros((n,) + tuple(case.key_cache.shape[1:]), dtype=case.key_cache.dtype)
+        runs, t = 0, 0.0
+        while t < 2.0 or runs == 0:
+            t0 = time.perf_counter()
+            oracle.copy_blocks(hs[0], hs[1], dst, dst.clone(), m)
+            t += time.perf_counter() - t0
+            runs += 1
+        result["cpu_baseline"] = {"value": round(moved / (t / runs) / 1e9, 3), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"the same {n} blocks copied on the host, {runs} runs"}
     print(json.dumps(result), flush=True)
 
 
