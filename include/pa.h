@@ -281,6 +281,97 @@ pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,
                          const int64_t *block_mapping, int32_t num_pairs, int64_t src_num_blocks,
                          int64_t dst_num_blocks, int64_t block_bytes, void *stream);
 
+/*
+ * Block manager (host side) -- the allocator that produces the block tables
+ * and slot mappings the kernels above read.
+ *
+ * The pool holds num_blocks physical blocks of block_size tokens.  Each
+ * sequence's block table maps its logical blocks to physical ones; a block
+ * carries a reference count; blocks come from a free pool on demand as a
+ * sequence grows and go back when it is freed ("vLLM High-Performance
+ * Inference Engine: PagedAttention Principles and Deployment Guide", section
+ * "PagedAttention Architecture Deep Dive"; "Configuring vLLM and
+ * PagedAttention for High Throughput Enterprise LLM Serving", section
+ * "Architectural Foundations: PagedAttention & Virtual Memory").  Sequences
+ * share blocks after a fork or through the prefix cache, and a write into a
+ * shared, partly filled block first copies it ("vLLM Guide: High-Throughput
+ * Multi-GPU LLM Serving with PagedAttention", section "What Is
+ * PagedAttention?": copy-on-write).  With enable_prefix_cache, every full
+ * block is indexed by a chained hash of the token ids of the sequence up to
+ * its end, and a new sequence whose prompt starts with the same full blocks
+ * reuses them (automatic prefix caching); reuse requires equal stored tokens
+ * and the same preceding physical block, never a hash match alone.
+ *
+ * Policy: the free pool is first-in first-out (blocks 0, 1, ... at first); a
+ * freed block that is in the prefix index stays reusable until the pool hands
+ * it out again.  All calls are host-only, synchronous and not thread-safe
+ * (one manager per scheduler thread).  Errors: PA_ERR_INVALID_ARG (bad
+ * argument or unknown / duplicate sequence id), PA_ERR_WORKSPACE (the pool
+ * has too few free blocks; nothing was changed).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+typedef struct pa_bm_stats {
+    int64_t num_blocks;     /* pool size */
+    int64_t free_blocks;    /* blocks in the free pool (cached ones included) */
+    int64_t used_blocks;    /* num_blocks - free_blocks */
+    int64_t shared_blocks;  /* blocks referenced more than once */
+    int64_t cached_blocks;  /* blocks in the prefix index */
+    int64_t num_seqs;
+    int64_t seq_tokens;     /* sum of sequence lengths */
+    int64_t seq_slots;      /* sum over sequences of table length x block_size */
+    int64_t prefix_hits;    /* blocks reused from the prefix index so far */
+} pa_bm_stats;
+
+/* Creates a manager over a pool of num_blocks blocks; *out owns it. */
+pa_status pa_bm_create(int64_t num_blocks, int32_t block_size, int32_t enable_prefix_cache,
+                       pa_block_manager **out);
+void pa_bm_destroy(pa_block_manager *bm);
+
+/*
+ * Registers sequence seq_id with its prompt (num_tokens token ids, host
+ * memory) and allocates its blocks.  slot_mapping[t] (host, num_tokens
+ * entries) receives the slot (block * block_size + offset) of prompt token t
+ * for pa_reshape_and_cache, or -1 when the token's block came from the prefix
+ * cache (its keys and values are already in the pool).  *num_cached_tokens
+ * (optional) receives that count.
+ */
+pa_status pa_bm_add_sequence(pa_block_manager *bm, int64_t seq_id, const int32_t *tokens,
+                             int32_t num_tokens, int64_t *slot_mapping,
+                             int32_t *num_cached_tokens);
+
+/*
+ * Appends one token to seq_id and returns its slot in *slot.  A new block is
+ * taken when the last one is full; when the last block is shared and partly
+ * filled, a new block replaces it in this sequence's table and the pair
+ * (old, new) is queued for pa_copy_blocks (see pa_bm_take_copies).
+ */
+pa_status pa_bm_append(pa_block_manager *bm, int64_t seq_id, int32_t token, int64_t *slot);
+
+/* child shares every block of parent (reference counts + 1). */
+pa_status pa_bm_fork(pa_block_manager *bm, int64_t parent, int64_t child);
+
+/* Drops seq_id; blocks whose count reaches 0 return to the free pool. */
+pa_status pa_bm_free(pa_block_manager *bm, int64_t seq_id);
+
+/*
+ * Moves the queued copy-on-write pairs (source block, destination block),
+ * int64 [n][2], into pairs and returns n.  If max_pairs < n (or pairs is
+ * NULL) nothing is moved and n is returned.  Run pa_copy_blocks on them
+ * before the step's cache write.  Returns -1 if bm is NULL.
+ */
+int32_t pa_bm_take_copies(pa_block_manager *bm, int64_t *pairs, int32_t max_pairs);
+
+/*
+ * The block table row of seq_id (row: max_blocks entries, host; may be NULL
+ * to query the sizes), its number of blocks and its context length.
+ */
+pa_status pa_bm_block_table(const pa_block_manager *bm, int64_t seq_id, int32_t *row,
+                            int32_t max_blocks, int32_t *num_blocks, int32_t *context_len);
+
+/* Pool statistics; internal fragmentation = 1 - seq_tokens / seq_slots. */
+pa_status pa_bm_get_stats(const pa_block_manager *bm, pa_bm_stats *stats);
+
 #ifdef __cplusplus
 }
 #endif

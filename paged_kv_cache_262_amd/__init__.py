@@ -7,6 +7,7 @@ caller's current HIP stream.  Nothing here computes attention; if the shared
 library is missing every entry point raises.
 """
 from .binding import (  # noqa: F401
+    BlockManager,
     PAError,
     copy_blocks,
     decode,

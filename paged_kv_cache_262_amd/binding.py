@@ -46,6 +46,15 @@ SIGNATURES = {
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
+    "pa_bm_create": (_i32, [_i64, _i32, _i32, _vp]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add_sequence": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
+    "pa_bm_append": (_i32, [_vp, _i64, _i32, _vp]),
+    "pa_bm_fork": (_i32, [_vp, _i64, _i64]),
+    "pa_bm_free": (_i32, [_vp, _i64]),
+    "pa_bm_take_copies": (_i32, [_vp, _vp, _i32]),
+    "pa_bm_block_table": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
+    "pa_bm_get_stats": (_i32, [_vp, _vp]),
 }
 
 
@@ -257,3 +266,75 @@ def copy_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, 
         src_key_cache.data_ptr(), src_value_cache.data_ptr(), dst_key_cache.data_ptr(),
         dst_value_cache.data_ptr(), block_mapping.data_ptr(), block_mapping.shape[0],
         src_key_cache.shape[0], dst_key_cache.shape[0], block_bytes, _stream(stream)))
+
+
+class _BmStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_blocks", "free_blocks", "used_blocks", "shared_blocks", "cached_blocks", "num_seqs",
+        "seq_tokens", "seq_slots", "prefix_hits")]
+
+
+class BlockManager:
+    """The library's host block manager (pa_bm_* in include/pa.h): block tables,
+    slot mappings, reference counts, copy-on-write pairs and the prefix cache."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_cache: bool = False):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_bm_create(num_blocks, block_size, int(prefix_cache), ctypes.byref(h)))
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq_id: int, tokens):
+        """Registers a sequence with its prompt; returns (slots, cached_tokens):
+        slots[t] is the slot of prompt token t, or -1 if its block was reused."""
+        toks = (ctypes.c_int32 * max(1, len(tokens)))(*tokens)
+        slots = (ctypes.c_int64 * max(1, len(tokens)))()
+        cached = ctypes.c_int32()
+        _check(self._lib.pa_bm_add_sequence(self._h, seq_id, toks, len(tokens), slots,
+                                            ctypes.byref(cached)))
+        return list(slots)[:len(tokens)], cached.value
+
+    def append(self, seq_id: int, token: int) -> int:
+        slot = ctypes.c_int64()
+        _check(self._lib.pa_bm_append(self._h, seq_id, token, ctypes.byref(slot)))
+        return slot.value
+
+    def fork(self, parent: int, child: int):
+        _check(self._lib.pa_bm_fork(self._h, parent, child))
+
+    def free(self, seq_id: int):
+        _check(self._lib.pa_bm_free(self._h, seq_id))
+
+    def take_copies(self):
+        n = self._lib.pa_bm_take_copies(self._h, None, 0)
+        if n <= 0:
+            return []
+        buf = (ctypes.c_int64 * (2 * n))()
+        got = self._lib.pa_bm_take_copies(self._h, buf, n)
+        assert got == n
+        return [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
+
+    def block_table(self, seq_id: int):
+        nb, L = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pa_bm_block_table(self._h, seq_id, None, 0, ctypes.byref(nb),
+                                           ctypes.byref(L)))
+        row = (ctypes.c_int32 * max(1, nb.value))()
+        _check(self._lib.pa_bm_block_table(self._h, seq_id, row, nb.value, None, None))
+        return list(row)[:nb.value], L.value
+
+    def stats(self) -> dict:
+        st = _BmStats()
+        _check(self._lib.pa_bm_get_stats(self._h, ctypes.byref(st)))
+        return {n: getattr(st, n) for n, _ in _BmStats._fields_}

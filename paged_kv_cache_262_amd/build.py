@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_262_amd.build
 
-Each .hip source is compiled by hipcc for gfx950 only (in parallel), then the
-objects are linked into paged_kv_cache_262_amd/libpa.so.  Packed fp32 VALU
+Each .hip source is compiled by hipcc for gfx950 only, and each .cpp source
+(host-only code) by the host C++ compiler, in parallel; the objects are linked
+into paged_kv_cache_262_amd/libpa.so.  Packed fp32 VALU
 instructions are disabled for device code.
 """
 from __future__ import annotations
@@ -31,15 +32,22 @@ CFLAGS = [
 ]
 
 
+HOST_CXX = os.environ.get("CXX_HOST", "g++")
+HOST_FLAGS = ["-std=c++17", "-O2", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    subprocess.run([HIPCC, *CFLAGS, "-c", src, "-o", obj], check=True)
+    if src.endswith(".cpp"):  # host-only code (the block manager)
+        subprocess.run([HOST_CXX, *HOST_FLAGS, "-c", src, "-o", obj], check=True)
+    else:
+        subprocess.run([HIPCC, *CFLAGS, "-c", src, "-o", obj], check=True)
     return obj
 
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
