@@ -369,6 +369,25 @@ int32_t pa_bm_take_copies(pa_block_manager *bm, int64_t *pairs, int32_t max_pair
 pa_status pa_bm_block_table(const pa_block_manager *bm, int64_t seq_id, int32_t *row,
                             int32_t max_blocks, int32_t *num_blocks, int32_t *context_len);
 
+/*
+ * One decode step for a batch: appends tokens[i] to seq_ids[i] (distinct
+ * ids) in order, as pa_bm_append, and writes the slots (the step's
+ * slot_mapping).  The blocks the step needs are checked first: on
+ * PA_ERR_WORKSPACE or PA_ERR_INVALID_ARG nothing has changed.
+ */
+pa_status pa_bm_append_batch(pa_block_manager *bm, const int64_t *seq_ids,
+                             const int32_t *tokens, int32_t n, int64_t *slots);
+
+/*
+ * The block tables of seq_ids as the kernels take them: tables is int32
+ * [n][max_blocks] (host), row i holds seq_ids[i]'s table padded with fill;
+ * context_lens (optional, int32 [n]) receives the lengths.  A table longer
+ * than max_blocks, or an unknown id, is PA_ERR_INVALID_ARG (nothing written).
+ */
+pa_status pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids, int32_t n,
+                             int32_t *tables, int32_t max_blocks, int32_t fill,
+                             int32_t *context_lens);
+
 /* Pool statistics; internal fragmentation = 1 - seq_tokens / seq_slots. */
 pa_status pa_bm_get_stats(const pa_block_manager *bm, pa_bm_stats *stats);
 

@@ -55,6 +55,8 @@ SIGNATURES = {
     "pa_bm_take_copies": (_i32, [_vp, _vp, _i32]),
     "pa_bm_block_table": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
     "pa_bm_get_stats": (_i32, [_vp, _vp]),
+    "pa_bm_append_batch": (_i32, [_vp, _vp, _vp, _i32, _vp]),
+    "pa_bm_block_tables": (_i32, [_vp, _vp, _i32, _vp, _i32, _i32, _vp]),
 }
 
 
@@ -333,6 +335,24 @@ class BlockManager:
         row = (ctypes.c_int32 * max(1, nb.value))()
         _check(self._lib.pa_bm_block_table(self._h, seq_id, row, nb.value, None, None))
         return list(row)[:nb.value], L.value
+
+    def append_batch(self, seq_ids, tokens) -> torch.Tensor:
+        """One step: tokens[i] appended to seq_ids[i]; returns the int64 slots."""
+        ids = torch.as_tensor(seq_ids, dtype=torch.int64).contiguous()
+        tok = torch.as_tensor(tokens, dtype=torch.int32).contiguous()
+        slots = torch.empty(ids.numel(), dtype=torch.int64)
+        _check(self._lib.pa_bm_append_batch(self._h, ids.data_ptr(), tok.data_ptr(), ids.numel(),
+                                            slots.data_ptr()))
+        return slots
+
+    def block_tables(self, seq_ids, max_blocks: int, fill: int = 0):
+        """(int32 [n, max_blocks] tables padded with fill, int32 [n] lengths)."""
+        ids = torch.as_tensor(seq_ids, dtype=torch.int64).contiguous()
+        tables = torch.empty((ids.numel(), max_blocks), dtype=torch.int32)
+        lens = torch.empty(ids.numel(), dtype=torch.int32)
+        _check(self._lib.pa_bm_block_tables(self._h, ids.data_ptr(), ids.numel(),
+                                            tables.data_ptr(), max_blocks, fill, lens.data_ptr()))
+        return tables, lens
 
     def stats(self) -> dict:
         st = _BmStats()

@@ -291,6 +291,49 @@ pa_status pa_bm_block_table(const pa_block_manager *bm, int64_t seq_id, int32_t 
     return PA_OK;
 }
 
+pa_status pa_bm_append_batch(pa_block_manager *bm, const int64_t *seq_ids,
+                             const int32_t *tokens, int32_t n, int64_t *slots) {
+    if (!bm || n < 0 || (n > 0 && (!seq_ids || !tokens || !slots))) return PA_ERR_INVALID_ARG;
+    // Blocks the step takes: a new block where the last one is full, a copy
+    // where it is shared and partly filled.  Checked up front, so a failed
+    // call changes nothing.
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end()) return PA_ERR_INVALID_ARG;
+        for (int32_t k = 0; k < i; ++k)
+            if (seq_ids[k] == seq_ids[i]) return PA_ERR_INVALID_ARG;  // one token per sequence
+        const Sequence &sq = it->second;
+        if (sq.len % bm->block_size == 0 || bm->blocks[sq.table.back()].ref > 1) ++need;
+    }
+    if (bm->free_count < need) return PA_ERR_WORKSPACE;
+    for (int32_t i = 0; i < n; ++i) {
+        const pa_status st = pa_bm_append(bm, seq_ids[i], tokens[i], slots + i);
+        if (st != PA_OK) return st;  // not reached: checked above
+    }
+    return PA_OK;
+}
+
+pa_status pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids, int32_t n,
+                             int32_t *tables, int32_t max_blocks, int32_t fill,
+                             int32_t *context_lens) {
+    if (!bm || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !tables))) return PA_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = bm->seqs.find(seq_ids[i]);
+        if (it == bm->seqs.end() || (int64_t)it->second.table.size() > max_blocks)
+            return PA_ERR_INVALID_ARG;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Sequence &sq = bm->seqs.find(seq_ids[i])->second;
+        int32_t *row = tables + (int64_t)i * max_blocks;
+        const int32_t nb = (int32_t)sq.table.size();
+        std::memcpy(row, sq.table.data(), sizeof(int32_t) * nb);
+        for (int32_t j = nb; j < max_blocks; ++j) row[j] = fill;
+        if (context_lens) context_lens[i] = (int32_t)sq.len;
+    }
+    return PA_OK;
+}
+
 pa_status pa_bm_get_stats(const pa_block_manager *bm, pa_bm_stats *st) {
     if (!bm || !st) return PA_ERR_INVALID_ARG;
     std::memset(st, 0, sizeof(*st));

@@ -169,3 +169,38 @@ def test_library_rejects_bad_calls():
         bm.add_sequence(2, list(range(16 * 8)))    # needs 8 blocks, 7 free: nothing changes
     assert bm.stats()["free_blocks"] == 7
     bm.close()
+
+
+def test_batch_calls_equal_single_calls():
+    rnd = random.Random(9)
+    a = binding.BlockManager(400, 8, prefix_cache=True)
+    ref = ReferenceBlockManager(400, 8, True)
+    base = [rnd.randint(0, 5) for _ in range(30)]
+    for s in range(10):
+        p = base[:rnd.randint(1, 30)] + [rnd.randint(0, 5) for _ in range(rnd.randint(0, 9))]
+        assert a.add_sequence(s, p) == ref.add_sequence(s, p)
+    a.fork(3, 10)
+    ref.fork(3, 10)
+    ids = list(range(11))
+    for _ in range(20):
+        toks = [rnd.randint(0, 5) for _ in ids]
+        slots = a.append_batch(ids, toks)
+        assert slots.tolist() == [ref.append(s, t) for s, t in zip(ids, toks)]
+        assert a.take_copies() == ref.take_copies()
+        tables, lens = a.block_tables(ids, 12, fill=-1)
+        for i, s in enumerate(ids):
+            t = ref.tables[s]
+            assert tables[i].tolist() == t + [-1] * (12 - len(t))
+            assert lens[i] == len(ref.tokens[s])
+    with pytest.raises(binding.PAError):
+        a.block_tables(ids, 2)                      # tables longer than 2 blocks
+    with pytest.raises(binding.PAError):
+        a.append_batch([1, 1], [0, 0])              # one token per sequence per step
+    small = binding.BlockManager(3, 4)
+    small.add_sequence(0, [1, 2, 3, 4])
+    small.add_sequence(1, [1, 2, 3, 4])
+    with pytest.raises(binding.PAError):
+        small.append_batch([0, 1], [5, 5])          # needs 2 blocks, 1 free: nothing changes
+    assert small.stats()["seq_tokens"] == 8 and small.stats()["free_blocks"] == 1
+    a.close()
+    small.close()
