@@ -134,3 +134,20 @@ def test_prefill_last_row_matches_decode():
                         c.chunk_context_lens, c.scale)
     check_close(pout[rows], ref, "bf16", "prefill last rows")
     check_close(dout, ref, "bf16", "decode of the same rows")
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_prefill_context_beyond_the_table_window(B):
+    """A chunk over a 40,000-token context: at 16-token blocks its tiles read
+    2,500 pages, more than the 2,048 block-table entries a tile keeps in LDS,
+    so the kernel refills that window mid-way (at 32-token blocks it does not:
+    the control case)."""
+    c = W.make_case("pf_long", 91 + B, "bf16", 8, 2, 128, B, [3], new_positions=[2],
+                    chunks=[(64, 40000)], extra_blocks=2)
+    kc, vc = dev(c.key_cache), dev(c.value_cache)
+    apply_cache_write_gpu(c, kc, vc)
+    say("prefill long context", B)
+    out = gpu_prefill(c, kc, vc)
+    torch.cuda.synchronize()
+    ref = oracle_prefill(c, *oracle_pools(c))
+    check_close(out, ref, "bf16", f"prefill 40K context B{B}")
