@@ -53,8 +53,16 @@ def load(path: str | None = None):
                                    i64, ctypes.c_float, i32]
     lib.oracle_reshape_and_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32]
     lib.oracle_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32]
+    f32 = ctypes.c_float
+    lib.oracle_fp8_encode.argtypes = [vp, i32, f32, vp]
+    lib.oracle_fp8_decode.argtypes = [vp, i32, vp]
+    lib.oracle_reshape_and_cache_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32,
+                                                 f32, f32]
+    lib.oracle_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                      f32, i32, f32, f32]
     for f in (lib.oracle_gather, lib.oracle_decode, lib.oracle_prefill,
-              lib.oracle_reshape_and_cache, lib.oracle_copy_blocks):
+              lib.oracle_reshape_and_cache, lib.oracle_copy_blocks, lib.oracle_fp8_encode,
+              lib.oracle_fp8_decode, lib.oracle_reshape_and_cache_fp8, lib.oracle_decode_fp8):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -152,3 +160,55 @@ def copy_blocks(src_key, src_value, dst_key, dst_value, block_mapping, lib=None)
     _check(lib.oracle_copy_blocks(_ptr(sk), _ptr(sv), _ptr(dk), _ptr(dv), _ptr(m), m.shape[0],
                                   sk.shape[0], dk.shape[0], block_bytes, int(in_place)))
     return dk, dv
+
+
+def fp8_encode(x, scale=1.0, lib=None):
+    """e4m3 codes (uint8 tensor) of x / scale (x: float tensor; see pa_oracle.c)."""
+    lib = lib or load()
+    xf = torch.as_tensor(x, dtype=torch.float32).contiguous().reshape(-1)
+    codes = torch.empty(xf.numel(), dtype=torch.uint8)
+    _check(lib.oracle_fp8_encode(_ptr(xf), xf.numel(), ctypes.c_float(scale), _ptr(codes)))
+    return codes.reshape(torch.as_tensor(x).shape)
+
+
+def fp8_decode(codes, lib=None):
+    """Values (float64 numpy) of e4m3 codes."""
+    lib = lib or load()
+    c = torch.as_tensor(codes, dtype=torch.uint8).contiguous().reshape(-1)
+    out = np.empty(c.numel(), dtype=np.float64)
+    _check(lib.oracle_fp8_decode(_ptr(c), c.numel(), out.ctypes.data))
+    return out.reshape(tuple(torch.as_tensor(codes).shape))
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                          lib=None):
+    """FP8 cache write into copies of the uint8 pools (K [NB, Hkv, B, D], V
+    [NB, Hkv, D, B]); returns (kc, vc)."""
+    lib = lib or load()
+    T, Hkv, D = key.shape
+    NB, Hkv2, B, D2 = key_cache.shape
+    assert Hkv == Hkv2 and D == D2 and tuple(value_cache.shape) == (NB, Hkv, D, B)
+    kc, vc = key_cache.clone().contiguous(), value_cache.clone().contiguous()
+    k, v = key.contiguous(), value.contiguous()
+    slots = torch.as_tensor(slot_mapping, dtype=torch.int64).contiguous()
+    _check(lib.oracle_reshape_and_cache_fp8(_ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(slots), T,
+                                            Hkv, D, B, NB, _DT[k.dtype], ctypes.c_float(k_scale),
+                                            ctypes.c_float(v_scale)))
+    return kc, vc
+
+
+def decode_fp8(query, key_cache, value_cache, block_tables, context_lens, scale, k_scale,
+               v_scale, lib=None):
+    """fp64 decode over FP8 pools (K [NB, Hkv, B, D], V [NB, Hkv, D, B])."""
+    lib = lib or load()
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = key_cache.shape
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    q = query.contiguous()
+    bt = block_tables.to(torch.int32).contiguous()
+    lens = context_lens.to(torch.int32).contiguous()
+    _check(lib.oracle_decode_fp8(out.ctypes.data, _ptr(q), _ptr(key_cache.contiguous()),
+                                 _ptr(value_cache.contiguous()), _ptr(bt), _ptr(lens), S, Hq, Hkv,
+                                 D, B, bt.shape[1], NB, ctypes.c_float(scale), _DT[q.dtype],
+                                 ctypes.c_float(k_scale), ctypes.c_float(v_scale)))
+    return out

@@ -375,3 +375,198 @@ int oracle_copy_blocks(const void *src_key, const void *src_value, void *dst_key
     free(snap_v);
     return 0;
 }
+
+/* ---- FP8 KV cache: e4m3 codes with a per-tensor scale -------------------- */
+
+/*
+ * Quantised KV cache ("vLLM Guide: High-Throughput Multi-GPU LLM Serving with
+ * PagedAttention", the pillars section's quantisation support, and the FP8
+ * engine example on the same page): every element is stored as an 8-bit
+ * floating-point code (OCP e4m3: 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, code S.1111.111 is NaN; largest finite value
+ * 448, smallest subnormal 2^-9) of x / scale, with one fp32 scale per pool.
+ * Readings (the pages give no rounding rule):
+ *   - x / scale is taken in fp32 as x * (1 / scale), both roundings fp32 RNE;
+ *   - the code is the nearest e4m3 value, ties to the even code, saturating
+ *     at +-448 (infinities included); NaN gives code 0x7F;
+ *   - the V pool of the FP8 cache is stored transposed per page,
+ *     [block][kv head][head_dim][block_size], the K pool as the bf16 one.
+ */
+static double e4m3_value(unsigned c)
+{
+    unsigned s = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -v : v;
+}
+
+static unsigned e4m3_encode(float y)
+{
+    if (y != y)
+        return 0x7F;
+    unsigned sign = signbit(y) ? 0x80u : 0u;
+    double a = fabs((double)y);
+    if (a > 448.0)
+        a = 448.0;
+    unsigned best = 0;
+    double best_d = INFINITY;
+    for (unsigned c = 0; c < 0x7F; ++c) {  /* every finite non-negative code */
+        double d = fabs(e4m3_value(c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | best;
+}
+
+int oracle_fp8_encode(const float *x, int n, float scale, unsigned char *codes)
+{
+    if (n < 0 || !(scale > 0.0f))
+        return 1;
+    float inv = 1.0f / scale;
+    for (int i = 0; i < n; ++i)
+        codes[i] = (unsigned char)e4m3_encode(x[i] * inv);
+    return 0;
+}
+
+int oracle_fp8_decode(const unsigned char *codes, int n, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = e4m3_value(codes[i]);
+    return 0;
+}
+
+/*
+ * Cache write into FP8 pools: as oracle_reshape_and_cache, with each element
+ * encoded as above; K goes to [block][head][offset][d], V to
+ * [block][head][d][offset].
+ */
+int oracle_reshape_and_cache_fp8(const void *key, const void *value, unsigned char *key_cache,
+                                 unsigned char *value_cache, const int64_t *slot_mapping,
+                                 int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                                 int64_t num_blocks, int dtype, float k_scale, float v_scale)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        !(k_scale > 0.0f) || !(v_scale > 0.0f))
+        return 1;
+    int64_t nslots = num_blocks * block_size;
+    unsigned char *seen = calloc((size_t)(nslots > 0 ? nslots : 1), 1);
+    if (!seen)
+        return 5;
+    for (int t = 0; t < num_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        if (s >= nslots || seen[s]) {
+            free(seen);
+            return s >= nslots ? 3 : 4;
+        }
+        seen[s] = 1;
+    }
+    free(seen);
+    float kinv = 1.0f / k_scale, vinv = 1.0f / v_scale;
+    for (int t = 0; t < num_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        if (s < 0)
+            continue;
+        int64_t blk = s / block_size;
+        int off = (int)(s % block_size);
+        for (int h = 0; h < num_kv_heads; ++h) {
+            size_t src = ((size_t)t * num_kv_heads + h) * head_dim;
+            size_t page = ((size_t)blk * num_kv_heads + h) * (size_t)block_size * head_dim;
+            for (int d = 0; d < head_dim; ++d) {
+                float k = (float)widen(key, src + d, dtype);
+                float v = (float)widen(value, src + d, dtype);
+                key_cache[page + (size_t)off * head_dim + d] = (unsigned char)e4m3_encode(k * kinv);
+                value_cache[page + (size_t)d * block_size + off] =
+                    (unsigned char)e4m3_encode(v * vinv);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Decode over FP8 pools: every element read is its code's value times the
+ * pool's scale (in fp64), then the same attention as oracle_decode.
+ */
+int oracle_decode_fp8(double *out, const void *query, const unsigned char *key_cache,
+                      const unsigned char *value_cache, const int32_t *block_tables,
+                      const int32_t *context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int block_size, int max_blocks,
+                      int64_t num_blocks, float scale, int q_dtype, float k_scale, float v_scale)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+        head_dim <= 0 || block_size <= 0)
+        return 1;
+    const int group = num_q_heads / num_kv_heads;
+    const int D = head_dim;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic) reduction(max : status)
+    for (int sh = 0; sh < num_seqs * num_q_heads; ++sh) {
+        int s = sh / num_q_heads, h = sh % num_q_heads, g = h / group;
+        int L = context_lens[s];
+        int err = 0;  /* this row's error; folded into status at the end */
+        double *o = out + (size_t)sh * D;
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        if (L <= 0)
+            continue;
+        double *K = malloc(sizeof(double) * (size_t)L * D), *V = malloc(sizeof(double) * (size_t)L * D);
+        double *q = malloc(sizeof(double) * D), *x = malloc(sizeof(double) * L);
+        if (!K || !V || !q || !x) {
+            err = 5;
+        } else {
+            const int32_t *row = block_tables + (size_t)s * max_blocks;
+            for (int j = 0; j < L && !err; ++j) {
+                int32_t phys = row[j / block_size];
+                int off = j % block_size;
+                if (phys < 0 || phys >= num_blocks) {
+                    err = 2;
+                    break;
+                }
+                size_t page = ((size_t)phys * num_kv_heads + g) * (size_t)block_size * D;
+                for (int d = 0; d < D; ++d) {
+                    K[(size_t)j * D + d] = e4m3_value(key_cache[page + (size_t)off * D + d]) * (double)k_scale;
+                    V[(size_t)j * D + d] = e4m3_value(value_cache[page + (size_t)d * block_size + off]) * (double)v_scale;
+                }
+            }
+            if (!err) {
+                for (int d = 0; d < D; ++d)
+                    q[d] = widen(query, ((size_t)s * num_q_heads + h) * D + d, q_dtype);
+                double m = -INFINITY;
+                for (int j = 0; j < L; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += q[d] * K[(size_t)j * D + d];
+                    x[j] = (double)scale * dot;
+                    if (x[j] > m)
+                        m = x[j];
+                }
+                double Z = 0.0;
+                for (int j = 0; j < L; ++j) {
+                    x[j] = exp(x[j] - m);
+                    Z += x[j];
+                }
+                for (int j = 0; j < L; ++j) {
+                    double w = x[j] / Z;
+                    for (int d = 0; d < D; ++d)
+                        o[d] += w * V[(size_t)j * D + d];
+                }
+            }
+        }
+        free(K);
+        free(V);
+        free(q);
+        free(x);
+        if (err > status)
+            status = err;
+    }
+    return status;
+}

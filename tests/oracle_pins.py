@@ -459,6 +459,99 @@ def pin_copy_blocks_rejects(lib):
             assert e.code == code, (pairs, e.code)
 
 
+# -------------------------------------------------------------- FP8 cache --
+
+def _e4m3_table():
+    """The 256 e4m3 values from the format's definition (OCP 8-bit floating
+    point, E4M3: exponent bias 7, no infinities, S.1111.111 is NaN)."""
+    vals = []
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 0xF and m == 7:
+            vals.append(math.nan)
+        elif e == 0:
+            vals.append(sign * m * 2.0 ** -9)
+        else:
+            vals.append(sign * (8 + m) * 2.0 ** (e - 10))
+    return vals
+
+
+def pin_fp8_code_values(lib):
+    want = _e4m3_table()
+    got = oracle.fp8_decode(torch.arange(256, dtype=torch.uint8), lib=lib)
+    for c in range(256):
+        assert (math.isnan(want[c]) and math.isnan(got[c])) or want[c] == got[c], c
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+    assert got[0x38] == 1.0 and math.copysign(1.0, got[0x80]) < 0
+
+
+def pin_fp8_encode_rounding(lib):
+    """Every finite value encodes to its own code; midpoints go to the even
+    code; overflow saturates at 448; NaN is 0x7F; the scale divides first."""
+    vals = _e4m3_table()
+    codes = [c for c in range(256) if not math.isnan(vals[c])]
+    enc = oracle.fp8_encode(torch.tensor([vals[c] for c in codes]), lib=lib)
+    assert enc.tolist() == codes
+    mids = torch.tensor([1.0625, 1.1875, 1.3125, 2.0 ** -9 * 0.5, 2.0 ** -9 * 1.5, 232.0, 464.0])
+    want = [0x38, 0x3A, 0x3A, 0x00, 0x02, 0x76, 0x7E]   # ties to the even code
+    assert oracle.fp8_encode(mids, lib=lib).tolist() == want
+    assert oracle.fp8_encode(-mids, lib=lib).tolist() == [0x80 | w for w in want]
+    sat = torch.tensor([449.0, 1000.0, 1e30, math.inf, -math.inf, math.nan])
+    assert oracle.fp8_encode(sat, lib=lib).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x7F]
+    x = torch.randn(500) * 37
+    assert torch.equal(oracle.fp8_encode(x, 4.0, lib=lib), oracle.fp8_encode(x * 0.25, lib=lib))
+    # the nearest code: no code value lies strictly closer than the chosen one
+    y = torch.randn(2000) * 50
+    e = oracle.fp8_encode(y, lib=lib)
+    dec = oracle.fp8_decode(e, lib=lib)
+    finite = np.array([v for v in vals[:0x7F]])
+    for yi, di in zip(y.tolist(), dec.tolist()):
+        a = min(abs(yi), 448.0)
+        assert abs(abs(di) - a) <= np.min(np.abs(finite - a)) + 0.0
+
+
+def pin_fp8_cache_write_layout(lib):
+    """K lands at [block][head][offset][d], V transposed at [block][head][d][offset],
+    each the code of value / scale; untouched bytes keep their value."""
+    NB, Hkv, B, D = 5, 2, 16, 64
+    key = torch.zeros(2, Hkv, D)
+    val = torch.zeros(2, Hkv, D)
+    key[0, 1, 3], val[0, 1, 3] = 1.0, 2.0    # token 0 -> slot 2 * 16 + 5
+    key[1, 0, 7], val[1, 0, 60] = -3.0, 0.5  # token 1 -> slot 4 * 16 + 0
+    kc0 = torch.full((NB, Hkv, B, D), 0xAA, dtype=torch.uint8)
+    vc0 = torch.full((NB, Hkv, D, B), 0xAA, dtype=torch.uint8)
+    kc, vc = oracle.reshape_and_cache_fp8(key, val, kc0, vc0, [2 * 16 + 5, 4 * 16], 0.5, 2.0,
+                                          lib=lib)
+    assert kc[2, 1, 5, 3] == 0x40 and vc[2, 1, 3, 5] == 0x38           # 2.0 and 1.0
+    assert kc[4, 0, 0, 7] == 0xCC and vc[4, 0, 60, 0] == 0x28          # -6.0 = -1.5 * 2^2, 0.25
+    assert kc[2, 1, 5, 0] == 0 and vc[2, 0, 0, 5] == 0                  # zeros of the rows
+    touched_k = torch.zeros_like(kc, dtype=torch.bool)
+    touched_k[2, :, 5, :] = True
+    touched_k[4, :, 0, :] = True
+    touched_v = torch.zeros_like(vc, dtype=torch.bool)
+    touched_v[2, :, :, 5] = True
+    touched_v[4, :, :, 0] = True
+    assert torch.all(kc[~touched_k] == 0xAA) and torch.all(vc[~touched_v] == 0xAA)
+
+
+def pin_fp8_decode_equals_dequantized_decode(lib):
+    """Decode over FP8 pools equals decode over float pools that hold the
+    dequantised values (code value x scale, exact in fp32 for these scales)."""
+    c = W.random_case(71, "bf16", 4, 8, 2, 64, 16, 1, 90, write_new=False)
+    NB, Hkv, B, D = c.key_cache.shape
+    ks, vs = 0.25, 0.5
+    kc8 = oracle.fp8_encode(c.key_cache.float(), ks, lib=lib)
+    vc8 = oracle.fp8_encode(c.value_cache.float(), vs, lib=lib).permute(0, 1, 3, 2).contiguous()
+    kf = torch.from_numpy(oracle.fp8_decode(kc8, lib=lib) * ks).float()
+    vf = torch.from_numpy(oracle.fp8_decode(vc8, lib=lib) * vs).float().permute(0, 1, 3, 2).contiguous()
+    q = c.query.float()
+    ref = oracle.decode(q, kf, vf, c.block_tables, c.context_lens, c.scale, lib=lib)
+    out = oracle.decode_fp8(q, kc8, vc8, c.block_tables, c.context_lens, c.scale, ks, vs,
+                            lib=lib)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_gather_page_examples,
     pin_decode_one_hot_page_examples,
@@ -480,4 +573,8 @@ ALL_PINS = [
     pin_copy_on_write_keeps_attention,
     pin_swap_round_trip,
     pin_copy_blocks_rejects,
+    pin_fp8_code_values,
+    pin_fp8_encode_rounding,
+    pin_fp8_cache_write_layout,
+    pin_fp8_decode_equals_dequantized_decode,
 ]

@@ -54,6 +54,12 @@ MUTATIONS = {
                        "memcpy((char *)value_cache + dst, (const char *)key + src, row_bytes);"),
     "write_keeps_duplicates": ("if (seen[s]) {", "if (0) {"),
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
+    "fp8_ties_to_odd": ("if (d < best_d || (d == best_d && (c & 1) == 0)) {",
+                        "if (d < best_d || (d == best_d && (c & 1) == 1)) {"),
+    "fp8_nan_saturates": ("    if (y != y)\n        return 0x7F;", "    if (y != y)\n        return 0x7E;"),
+    "fp8_v_not_transposed": ("value_cache[page + (size_t)d * block_size + off] =",
+                             "value_cache[page + (size_t)off * head_dim + d] ="),
+    "fp8_subnormal_exponent": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
     "copy_v_from_k": ("memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_value + src,",
                       "memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_key + src,"),
     "copy_wrong_source": ("size_t src = (size_t)mapping[2 * i] * (size_t)block_bytes;",
