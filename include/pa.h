@@ -282,6 +282,72 @@ pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,
                          int64_t dst_num_blocks, int64_t block_bytes, void *stream);
 
 /*
+ * FP8 KV cache -- pools of 8-bit e4m3 codes, half the bytes of bf16.
+ *
+ * The pages list quantised KV caches among the engine's features and run an
+ * FP8 KV cache in their engine example ("vLLM Guide: High-Throughput
+ * Multi-GPU LLM Serving with PagedAttention", the quantisation support among
+ * the pillars of the engine, and the FP8 engine example); they give no format
+ * detail, so the following is this library's reading.
+ *
+ * Format: every element is one byte, the OCP e4m3 code (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN; largest
+ * finite 448, smallest subnormal 2^-9) of x / scale, with one fp32 scale per
+ * pool (k_scale for K, v_scale for V).  Encoding: y = x * (1 / scale) in
+ * fp32, then the nearest e4m3 value, ties to the even code, saturating at
+ * +-448; NaN -> 0x7F.  Decoding: value = code's value * scale.
+ *
+ * Layouts (uint8):
+ *   key_cache   : [num_blocks][num_kv_heads][block_size][head_dim] (as bf16)
+ *   value_cache : [num_blocks][num_kv_heads][head_dim][block_size] -- each
+ *                 page transposed, so a dim's tokens are contiguous.
+ * The page size is block_size * head_dim bytes.
+ */
+
+/*
+ * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into FP8 pools: for every
+ * t with slot_mapping[t] >= 0, the e4m3 codes of key[t][h][:] / k_scale go to
+ * key_cache[block][h][offset][:] and those of value[t][h][:] / v_scale to
+ * value_cache[block][h][:][offset].  key, value: [num_tokens][num_kv_heads]
+ * [head_dim] in dtype (PA_F32 or PA_BF16).  Scales must be positive and
+ * finite (PA_ERR_INVALID_ARG).  Other conventions as pa_reshape_and_cache.
+ */
+pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache,
+                                   void *value_cache, const int64_t *slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int64_t num_blocks, int32_t dtype,
+                                   float k_scale, float v_scale, void *stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over FP8 pools: the same attention, with
+ * K_s[j] and V_s[j] the decoded codes times k_scale and v_scale.  query and
+ * out are bf16 [num_seqs][num_q_heads][head_dim]; arithmetic is fp32 with
+ * both products on the bf16 matrix cores (the codes widen to bf16 exactly).
+ * Always the balanced split (no partition_size); num_seqs <= 8192
+ * (PA_ERR_UNSUPPORTED otherwise).  The workspace is
+ * pa_decode_workspace_bytes(..., partition_size = 0).  Other conventions,
+ * errors and the context-length rules as pa_decode.
+ * pa_decode_fp8_partitions is its first phase; pa_decode_reduce with
+ * partition_size 0 and dtype PA_BF16 completes it.
+ */
+pa_status pa_decode_fp8(void *out, const void *query, const void *key_cache,
+                        const void *value_cache, const int32_t *block_tables,
+                        const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                        float scale, float k_scale, float v_scale, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, int32_t max_context_len, float scale,
+                                   float k_scale, float v_scale, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
  * Block manager (host side) -- the allocator that produces the block tables
  * and slot mappings the kernels above read.
  *

@@ -46,6 +46,12 @@ SIGNATURES = {
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
+    "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
+                                        _i32, _f, _f, _vp]),
+    "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                             _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
+    "pa_decode_fp8_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, _i32, _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
     "pa_bm_create": (_i32, [_i64, _i32, _i32, _vp]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_sequence": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
@@ -230,6 +236,70 @@ def decode_append_partitions(out, query, new_key, new_value, key_cache, value_ca
         *_append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
                       context_lens, max_context_len, partition_size, scale, workspace),
         _stream(stream)))
+
+
+def _fp8_pools(key_cache, value_cache):
+    """Shape of FP8 pools: K uint8 [NB, Hkv, B, D], V uint8 [NB, Hkv, D, B]."""
+    if key_cache.dtype != torch.uint8 or value_cache.dtype != torch.uint8:
+        raise ValueError("FP8 pools hold uint8 e4m3 codes")
+    NB, Hkv, B, D = key_cache.shape
+    if tuple(value_cache.shape) != (NB, Hkv, D, B):
+        raise ValueError(f"value_cache must be [{NB}, {Hkv}, {D}, {B}] (pages transposed)")
+    return NB, Hkv, B, D
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                          stream=None):
+    """Quantising cache write: e4m3 codes of key / k_scale and value / v_scale at the slots."""
+    T, Hkv, D = key.shape
+    NB, _, B, _ = _fp8_pools(key_cache, value_cache)
+    if slot_mapping.dtype != torch.int64:
+        raise ValueError("slot_mapping must be int64")
+    _check(load().pa_reshape_and_cache_fp8(
+        _dev(key, "key"), _dev(value, "value"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping"), T, Hkv, D, B, NB,
+        _dtype(key), float(k_scale), float(v_scale), _stream(stream)))
+
+
+def _fp8_decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                     max_context_len, scale, k_scale, v_scale, workspace):
+    S, Hq, D = query.shape
+    NB, Hkv, B, _ = _fp8_pools(key_cache, value_cache)
+    if query.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("FP8 decode takes a bf16 query and writes a bf16 output")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    return (_dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+            _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+            _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, block_tables.shape[1], NB,
+            int(max_context_len), float(scale), float(k_scale), float(v_scale),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size())
+
+
+def make_fp8_workspace(query, key_cache, max_context_len):
+    S, Hq, D = query.shape
+    Hkv, B = key_cache.shape[1], key_cache.shape[2]
+    n = decode_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, 0)
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+               max_context_len, k_scale, v_scale, workspace=None, stream=None):
+    """Decode over FP8 pools (see reshape_and_cache_fp8); writes bf16 ``out`` [S, Hq, D]."""
+    if workspace is None:
+        workspace = make_fp8_workspace(query, key_cache, max_context_len)
+    _check(load().pa_decode_fp8(*_fp8_decode_args(out, query, key_cache, value_cache,
+                                                  block_tables, context_lens, max_context_len,
+                                                  scale, k_scale, v_scale, workspace),
+                                _stream(stream)))
+    return out
+
+
+def decode_fp8_partitions(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                          max_context_len, k_scale, v_scale, workspace, stream=None):
+    _check(load().pa_decode_fp8_partitions(*_fp8_decode_args(
+        out, query, key_cache, value_cache, block_tables, context_lens, max_context_len, scale,
+        k_scale, v_scale, workspace), _stream(stream)))
 
 
 def prefill_chunk(out, query, key_cache, value_cache, block_tables, cu_query_lens,

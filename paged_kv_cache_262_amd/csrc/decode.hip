@@ -954,6 +954,253 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
     if (cur_item >= 0) finish();
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split over an FP8 (e4m3) cache: the same work split, records and
+// reduce as decode_stream_mma_kernel, reading one byte per element.
+//
+// Every element of the pools is an e4m3 code of value / scale, with one fp32
+// scale per pool (quantised KV cache: "vLLM Guide: High-Throughput Multi-GPU
+// LLM Serving with PagedAttention", the quantisation support among the
+// engine's pillars and its FP8 engine example).  An e4m3 value has a 3-bit
+// mantissa and an exponent inside bf16's range, so every code widens to bf16
+// exactly (v_cvt_scalef32_pk_bf16_fp8 with a unit scale); the pools' scales
+// are applied outside the products: k_scale inside the softmax scale, v_scale
+// on the output.  Both products then run on the bf16 matrix cores exactly as
+// in the kernel above.
+//
+// Layouts.  K: [block][kv head][token][dim], a unit of 16 tokens is 16 * D
+// contiguous bytes.  V: [block][kv head][dim][token] (each page transposed),
+// so the V^T operand of the P V product (dim x 4 consecutive tokens per lane)
+// is one 4-byte load per lane and tile, with no transpose through LDS.
+//   K operand, k-step ks: lane (l16, lg) holds token l16, dims lg * D/4 + 8 ks
+//     + [0, 8) -- one contiguous D/4-byte piece of the token's row per lane;
+//     the Q^T operand takes the same dims, so the contraction is unchanged.
+//   V^T operand, tile dt: lane (l16, lg) holds dim dt * 16 + l16, tokens
+//     4 lg + [0, 4).
+// K rows past the unit's valid tokens come back as zeros (buffer range); in V
+// they share a row with valid tokens, so a partial unit masks its bytes.
+// ---------------------------------------------------------------------------
+
+#ifndef PA_FP8_BUFFERS
+#define PA_FP8_BUFFERS 5
+#endif
+constexpr int kFp8Buffers = PA_FP8_BUFFERS;  // units in flight + 1 per wave
+constexpr int kFp8Waves = 4;                 // waves per workgroup
+
+// Two e4m3 codes (bytes 0-1, or 2-3 when HI) -> two bf16, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
+    bf16_t *__restrict__ out, const bf16_t *__restrict__ query,
+    const uint8_t *__restrict__ key_cache, const uint8_t *__restrict__ value_cache,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens, int S,
+    int num_q_heads, int num_kv_heads, int max_blocks, int max_tokens, int64_t num_blocks, int nw,
+    float scale_log2, float v_scale, float *__restrict__ rec_o, float *__restrict__ rec_ml,
+    int *__restrict__ ws_scan) {
+    constexpr int KS = D / 32, DT = D / 16, KB = D / 4, KW = KB / 16;
+    constexpr int NB = kFp8Buffers;
+    static_assert(G <= 16, "group fits the 16 columns");
+    extern __shared__ int scan[];  // [S + 1], sized at launch
+    scan_units<NW>(scan, context_lens, S, max_tokens);
+    const int Hkv = num_kv_heads;
+    const int64_t U = (int64_t)scan[S] * Hkv;
+    if (blockIdx.x == 0)
+        for (int s = threadIdx.x; s <= S; s += NW * 64) ws_scan[s] = scan[s];
+
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int nwe = (int)min((int64_t)nw, U);
+    const int gw = blockIdx.x * NW + w;
+    if (gw >= nwe) return;
+    const int64_t ua = U * gw / nwe, ub = U * (gw + 1) / nwe;
+
+    const int64_t head_bytes = (int64_t)B * D;
+    const int64_t block_bytes = head_bytes * Hkv;
+    const char *kbase = (const char *)key_cache;
+    const char *vbase = (const char *)value_cache;
+    const int k_off = l16 * D + lg * KB;  // from the unit's first K row
+    const int v_off = l16 * B + lg * 4;   // from the unit's first token of dim 0
+    const s16x4_mv ones_a = l16 == 0 ? s16x4_mv{0x3F80, 0x3F80, 0x3F80, 0x3F80} : s16x4_mv{0, 0, 0, 0};
+
+    u32x4 qt[KS];
+    f32x4_mv acc_o[DT];
+    f32x4_mv acc_l;
+    float m_col = NEG_INF;
+    int cur_item = -1, cur_s = 0, cur_g = 0;
+
+    auto reset = [&](int s, int g) __attribute__((always_inline)) {
+        const bool valid = l16 < G;
+        const char *qrow = (const char *)query +
+                           ((int64_t)s * num_q_heads + (int64_t)g * G + (valid ? l16 : 0)) * (D * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = *(const u32x4 *)(qrow + (lg * KB + 8 * ks) * 2);
+            qt[ks] = valid ? v : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x4_mv{0.f, 0.f, 0.f, 0.f};
+        acc_l = f32x4_mv{0.f, 0.f, 0.f, 0.f};
+        m_col = NEG_INF;
+    };
+
+    auto finish = [&]() __attribute__((always_inline)) {
+        const int us = scan[cur_s + 1] - scan[cur_s];
+        const int64_t u0 = (int64_t)scan[cur_s] * Hkv + (int64_t)cur_g * us;
+        const bool whole = u0 >= ua && u0 + us <= ub;
+        const float lsum = __shfl(acc_l[0], l16);
+        if (l16 >= G) return;
+        const int64_t qrow = (int64_t)cur_s * num_q_heads + (int64_t)cur_g * G + l16;
+        if (whole) {
+            const float inv = lsum > 0.f ? v_scale / lsum : 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                uint2 v;
+                v.x = pack_bf16x2(acc_o[dt][0] * inv, acc_o[dt][1] * inv);
+                v.y = pack_bf16x2(acc_o[dt][2] * inv, acc_o[dt][3] * inv);
+                *(uint2 *)(out + qrow * D + dt * 16 + lg * 4) = v;
+            }
+        } else {
+            const int64_t rid = (int64_t)(cur_item + gw) * G + l16;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *(float4 *)(rec_o + rid * D + dt * 16 + lg * 4) =
+                    make_float4(acc_o[dt][0] * v_scale, acc_o[dt][1] * v_scale,
+                                acc_o[dt][2] * v_scale, acc_o[dt][3] * v_scale);
+            if (lg == 0) *(float2 *)(rec_ml + rid * 2) = make_float2(m_col, lsum);
+        }
+    };
+
+    for (int64_t base = ua; base < ub; base += 64) {
+        const int n = (int)min((int64_t)64, ub - base);
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0;
+        if (lane < n) {
+            const int64_t u = base + lane;
+            const int s = seq_of_unit(scan, S, u, Hkv);
+            const int us = scan[s + 1] - scan[s];
+            const int rem = (int)(u - (int64_t)scan[s] * Hkv);
+            const int g = rem / us;
+            const int j = rem - g * us;
+            l_item = s * Hkv + g;
+            const int L = clamp_len(context_lens[s], max_tokens);
+            const int tok = j * kUnitTokens;
+            l_nvalid = min(kUnitTokens, L - tok);
+            l_tokoff = tok % B;
+            const int phys = block_tables[(int64_t)s * max_blocks + tok / B];
+            if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
+            l_phys = phys;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
+
+        // Issue unit i of the chunk into buffer b.  Units past the segment get
+        // empty ranges: no memory is touched and zeros land.
+        u32x4 kb[NB][KW];
+        uint32_t vb[NB][DT];
+        int nv[NB];
+        auto issue = [&](int b, int i, int seg_end) __attribute__((always_inline)) {
+            const int ii = i & 63;
+            const int nvalid = (i < seg_end) ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
+            const int item = __builtin_amdgcn_readlane(l_item, ii);
+            const int phys = __builtin_amdgcn_readlane(l_phys, ii);
+            const int tokoff = __builtin_amdgcn_readlane(l_tokoff, ii);
+            const int64_t page = nvalid > 0 ? (int64_t)phys * block_bytes + (int64_t)(item % Hkv) * head_bytes : 0;
+            nv[b] = nvalid;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(kbase + page + (int64_t)tokoff * D), (short)0, nvalid > 0 ? nvalid * D : 0,
+                0x00020000);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(vbase + page + tokoff), (short)0, nvalid > 0 ? (D - 1) * B + kUnitTokens : 0,
+                0x00020000);
+#pragma unroll
+            for (int c = 0; c < KW; ++c)
+                kb[b][c] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + c * 16, 0, 0));
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                vb[b][dt] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_off + dt * 16 * B, 0, 0);
+        };
+
+        auto process = [&](int b) __attribute__((always_inline)) {
+            f32x4_mv st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint32_t w0 = kb[b][ks >> 1][(ks & 1) * 2];
+                const uint32_t w1 = kb[b][ks >> 1][(ks & 1) * 2 + 1];
+                const u32x4 kop = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                   e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)};
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_mv, kop),
+                                                             __builtin_bit_cast(bf16x8_mv, qt[ks]),
+                                                             st, 0, 0, 0);
+            }
+            float x[4];
+            bool need = m_col == NEG_INF;
+            float lmax = NEG_INF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (4 * lg + i < nv[b]) ? st[i] * scale_log2 : NEG_INF;
+                lmax = fmaxf(lmax, x[i]);
+            }
+            need |= lmax > m_col + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = fmaxf(m_col, max4_lanes(lmax));
+                const float alpha = (m_col == NEG_INF) ? 0.f : fast_exp2(m_col - mn);
+                m_col = mn;
+                acc_l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+            }
+            const float mneg = (m_col == NEG_INF) ? 0.f : -m_col;
+            const uint32_t p01 = pack_bf16x2(fast_exp2(x[0] + mneg), fast_exp2(x[1] + mneg));
+            const uint32_t p23 = pack_bf16x2(fast_exp2(x[2] + mneg), fast_exp2(x[3] + mneg));
+            const s16x4_mv pt = __builtin_bit_cast(s16x4_mv, (uint64_t)p01 | ((uint64_t)p23 << 32));
+            acc_l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones_a, pt, acc_l, 0, 0, 0);
+            // Tokens past the valid ones share their 4-byte words with valid
+            // tokens; their codes (stale or poison) must not reach the product.
+            uint32_t vmask = 0xFFFFFFFFu;
+            if (nv[b] < kUnitTokens) {
+                const int cnt = min(max(nv[b] - 4 * lg, 0), 4);
+                vmask = cnt == 4 ? 0xFFFFFFFFu : ((1u << (8 * cnt)) - 1u);
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint32_t wv = vb[b][dt] & vmask;
+                const s16x4_mv va = __builtin_bit_cast(
+                    s16x4_mv, (uint64_t)e4m3x2_to_bf16x2<false>(wv) |
+                                  ((uint64_t)e4m3x2_to_bf16x2<true>(wv) << 32));
+                acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pt, acc_o[dt], 0, 0, 0);
+            }
+        };
+
+        for (int i0 = 0; i0 < n;) {
+            const int item = __builtin_amdgcn_readlane(l_item, i0);
+            const uint64_t other =
+                __builtin_amdgcn_ballot_w64(lane < n && lane > i0 && l_item != item);
+            const int i1 = other ? (int)__builtin_ctzll(other) : n;  // segment end
+            if (item != cur_item) {
+                if (cur_item >= 0) finish();
+                cur_item = item;
+                cur_s = item / Hkv;
+                cur_g = item - cur_s * Hkv;
+                reset(cur_s, cur_g);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) issue(b, i0 + b, i1);
+            for (int i = i0; i < i1; i += NB) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (nv[b] > 0) process(b);
+                    issue(b, i + NB + b, i1);
+                }
+            }
+            i0 = i1;
+        }
+    }
+    if (cur_item >= 0) finish();
+}
+
 // Merge the nrec partial records (m_k: max in log2 units, l_k: sum, o_k:
 // unnormalised output) of one output row: with M = max_k m_k,
 // dst = sum_k o_k 2^(m_k - M) / sum_k l_k 2^(m_k - M) (log-sum-exp merge of
@@ -1229,8 +1476,26 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, int B, int G>
+static hipError_t launch_stream_fp8(const DecodeArgs &a, hipStream_t stream) {
+    const dim3 grid(cdiv(a.stream_waves, kFp8Waves));
+    const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
+    hipLaunchKernelGGL((decode_stream_fp8_kernel<D, B, G, kFp8Waves>), grid, dim3(kFp8Waves * 64),
+                       dyn, stream, (bf16_t *)a.out, (const bf16_t *)a.query,
+                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache,
+                       a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
+                       a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                       a.scale * kLog2e * a.k_scale, a.v_scale, a.ws_o, a.ws_ml, a.ws_scan);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int B, int G>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
+    if (a.kv_fp8) {  // bf16 query and output over e4m3 pools, balanced split only
+        if constexpr (std::is_same<T, bf16_t>::value)
+            if (a.stream_waves > 0 && !a.new_key) return launch_stream_fp8<D, B, G>(a, stream);
+        return hipErrorNotSupported;
+    }
     if (PA_DECODE_MMA && std::is_same<T, bf16_t>::value && a.stream_waves > 0)
         return launch_stream_mma<D, B, G>(a, stream);
     if (a.stream_waves > 0) {

@@ -174,6 +174,9 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
     a.dtype = dtype;
     a.new_key = nullptr;
     a.new_value = nullptr;
+    a.kv_fp8 = 0;
+    a.k_scale = 1.0f;
+    a.v_scale = 1.0f;
     char *ws = (char *)workspace;
     a.ws_o = uses_ws ? (float *)ws : nullptr;
     a.ws_ml = uses_ws ? (float *)(ws + plan.o_bytes) : nullptr;
@@ -365,6 +368,79 @@ pa_status pa_decode_append(void *out, const void *query, const void *new_key,
     return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             block_size, max_blocks_per_seq, max_context_len, partition_size,
                             dtype, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache,
+                                   void *value_cache, const int64_t *slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int64_t num_blocks, int32_t dtype,
+                                   float k_scale, float v_scale, void *stream) {
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+    if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads <= 0");
+    if (dtype != PA_F32 && dtype != PA_BF16)
+        return fail(PA_ERR_UNSUPPORTED, "dtype %d of the new rows not supported", dtype);
+    if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32))
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d / block_size %d not supported", head_dim,
+                    block_size);
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+    if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
+    if (num_tokens == 0) return PA_OK;
+    CHECK_PTR(key, 16);
+    CHECK_PTR(value, 16);
+    CHECK_PTR(key_cache, 16);
+    CHECK_PTR(value_cache, 16);
+    CHECK_PTR(slot_mapping, 8);
+    return hip_status(pa::launch_reshape_and_cache_fp8(
+                          key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                          num_kv_heads, head_dim, block_size, num_blocks,
+                          dtype == PA_BF16 ? 2 : 4, 1.0f / k_scale, 1.0f / v_scale,
+                          (hipStream_t)stream),
+                      "reshape_and_cache_fp8");
+}
+
+pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, int32_t max_context_len, float scale,
+                                   float k_scale, float v_scale, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (num_seqs > pa::kStreamMaxSeqs)
+        return fail(PA_ERR_UNSUPPORTED, "FP8 decode handles up to %d sequences per call",
+                    pa::kStreamMaxSeqs);
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, query, key_cache, value_cache, block_tables,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, num_blocks, max_context_len, 0,
+                               scale, PA_BF16, workspace, workspace_bytes, true);
+    if (s != PA_OK) return s;
+    st.a.kv_fp8 = 1;
+    st.a.k_scale = k_scale;
+    st.a.v_scale = v_scale;
+    return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
+                      "decode_fp8_partitions");
+}
+
+pa_status pa_decode_fp8(void *out, const void *query, const void *key_cache,
+                        const void *value_cache, const int32_t *block_tables,
+                        const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
+                        float scale, float k_scale, float v_scale, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    pa_status s = pa_decode_fp8_partitions(out, query, key_cache, value_cache, block_tables,
+                                           context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                           head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                           max_context_len, scale, k_scale, v_scale, workspace,
+                                           workspace_bytes, stream);
+    if (s != PA_OK) return s;
+    return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, max_context_len, 0, PA_BF16,
+                            workspace, workspace_bytes, stream);
 }
 
 pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,

@@ -17,6 +17,16 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *ke
 // into the slot of position context_lens[s] - 1; sequences whose length is 0
 // or above max_tokens, or whose block-table entry is outside the pool, are
 // skipped.
+// Cache write into e4m3 pools: element x of a new row is stored as the
+// e4m3 code of x * inv_scale (fp32 multiply, round to nearest even,
+// saturating at +-448, NaN -> 0x7F); K at [blk][h][off][d], V at
+// [blk][h][d][off].  elem_bytes (4 or 2) is that of the new rows.
+hipError_t launch_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache,
+                                        void *value_cache, const int64_t *slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int64_t num_blocks, int elem_bytes,
+                                        float k_inv_scale, float v_inv_scale, hipStream_t stream);
+
 hipError_t launch_append_rows(const void *key, const void *value, void *key_cache,
                               void *value_cache, const int32_t *block_tables,
                               const int32_t *context_lens, int num_seqs, int num_kv_heads,
@@ -58,6 +68,10 @@ struct DecodeArgs {
     // Non-null: the step's new token of each sequence ([S][Hkv][D]) is written
     // at position context_lens[s] - 1 and attended to (decode with append).
     const void *new_key, *new_value;
+    // Nonzero: the pools hold e4m3 codes (K [NB][Hkv][B][D], V [NB][Hkv][D][B])
+    // of value / k_scale and value / v_scale; query and output are bf16.
+    int kv_fp8;
+    float k_scale, v_scale;
 };
 
 // Copies block mapping[2i] of the source pools to block mapping[2i + 1] of the

@@ -53,6 +53,102 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *ke
     return hipGetLastError();
 }
 
+// ---- FP8 (e4m3) cache write ---------------------------------------------------
+//
+// Quantised KV cache ("vLLM Guide: High-Throughput Multi-GPU LLM Serving with
+// PagedAttention", the quantisation support among the engine's pillars and
+// its FP8 engine example): each element is kept as an 8-bit e4m3 code (sign,
+// 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+// NaN; largest finite 448, smallest subnormal 2^-9) of x / scale, one fp32
+// scale per pool.  The pages fix no rounding: x / scale is taken as one fp32
+// multiply by 1 / scale (computed on the host), then rounded to the nearest
+// e4m3 value, ties to the even code, saturating at +-448; NaN gives 0x7F.
+
+// e4m3 code of y, from the format's definition (no hardware conversion, so
+// the saturation and NaN rules above hold whatever the instruction does).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t u = __float_as_uint(y);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7Fu;  // NaN
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fminf(__uint_as_float(u & 0x7fffffffu), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        // below 2^-6: subnormal codes 0..7 step 2^-9 (8 rounds up to 2^-6)
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        // normal: keep 3 of fp32's 23 mantissa bits, round half to even; a
+        // carry moves into the exponent.  Rebias the exponent 127 -> 7.
+        uint32_t b = __float_as_uint(a);
+        b += 0x7FFFFu + ((b >> 20) & 1u);
+        code = (b >> 20) - (120u << 3);
+    }
+    return sign | code;
+}
+
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float (&x)[4]) {
+    if constexpr (sizeof(T) == 4) {
+        const float4 v = *(const float4 *)p;
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else {
+        const uint2 v = *(const uint2 *)p;
+        x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    }
+}
+
+// One workgroup per new token; a thread takes 4 consecutive dims of one kv
+// head: one 4-byte store into the K row, four byte stores down the dims of
+// the transposed V page.
+template <typename T>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const T *__restrict__ key, const T *__restrict__ value, uint8_t *__restrict__ key_cache,
+    uint8_t *__restrict__ value_cache, const int64_t *__restrict__ slot_mapping, int num_kv_heads,
+    int head_dim, int block_size, int64_t num_slots, float k_inv, float v_inv) {
+    const int t = blockIdx.x;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_slots) return;  // padding (or a caller error)
+    const int64_t blk = slot / block_size;
+    const int off = (int)(slot - blk * block_size);
+    const int quads = head_dim / 4;
+    for (int i = threadIdx.x; i < num_kv_heads * quads; i += blockDim.x) {
+        const int h = i / quads, d0 = (i - h * quads) * 4;
+        const int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + d0;
+        const int64_t page = (blk * num_kv_heads + h) * (int64_t)block_size * head_dim;
+        float k[4], v[4];
+        load4(key + src, k);
+        load4(value + src, v);
+        uint32_t kw = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kw |= e4m3_code(k[e] * k_inv) << (8 * e);
+        *(uint32_t *)(key_cache + page + (int64_t)off * head_dim + d0) = kw;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            value_cache[page + (int64_t)(d0 + e) * block_size + off] = (uint8_t)e4m3_code(v[e] * v_inv);
+    }
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void *key, const void *value, void *key_cache,
+                                        void *value_cache, const int64_t *slot_mapping,
+                                        int num_tokens, int num_kv_heads, int head_dim,
+                                        int block_size, int64_t num_blocks, int elem_bytes,
+                                        float k_inv_scale, float v_inv_scale, hipStream_t stream) {
+    const int per_token = num_kv_heads * head_dim / 4;
+    const int threads = per_token >= 256 ? 256 : ((per_token + 63) / 64) * 64;
+    if (elem_bytes == 4)
+        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, dim3(num_tokens), dim3(threads), 0,
+                           stream, (const float *)key, (const float *)value,
+                           (uint8_t *)key_cache, (uint8_t *)value_cache, slot_mapping,
+                           num_kv_heads, head_dim, block_size, num_blocks * block_size,
+                           k_inv_scale, v_inv_scale);
+    else
+        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, dim3(num_tokens), dim3(threads),
+                           0, stream, (const bf16_t *)key, (const bf16_t *)value,
+                           (uint8_t *)key_cache, (uint8_t *)value_cache, slot_mapping,
+                           num_kv_heads, head_dim, block_size, num_blocks * block_size,
+                           k_inv_scale, v_inv_scale);
+    return hipGetLastError();
+}
+
 // The new token of sequence s goes to position context_lens[s] - 1, whose slot
 // is block_tables[s][(L - 1) / B] at offset (L - 1) % B.  One workgroup per
 // sequence.

@@ -291,3 +291,16 @@ def random_case(seed: int, dtype: str, num_seqs: int, num_q_heads: int, num_kv_h
     return make_case(f"random_{seed}", seed, dtype, num_q_heads, num_kv_heads, head_dim,
                      block_size, lens, new_positions=newpos, extra_blocks=extra_blocks,
                      chunks=chunks, gen=gen)
+
+
+def random_fp8_codes(seed: int, shape, exp_lo: int = 3, exp_hi: int = 9) -> torch.Tensor:
+    """Seeded random e4m3 byte codes for FP8 pools: sign and 3 mantissa bits
+    uniform, the 4-bit exponent field uniform in [exp_lo, exp_hi] (values of
+    magnitude 2^(exp_lo - 7) .. 2^(exp_hi - 6), the spread of N(0, 1) data).
+    No NaN code (exponent field 15) is drawn for these defaults.  Only random
+    bits: the codes are not a quantisation of anything."""
+    gen = torch.Generator().manual_seed(seed)
+    sign = torch.randint(0, 2, shape, generator=gen, dtype=torch.int32)
+    expo = torch.randint(exp_lo, exp_hi + 1, shape, generator=gen, dtype=torch.int32)
+    mant = torch.randint(0, 8, shape, generator=gen, dtype=torch.int32)
+    return ((sign << 7) | (expo << 3) | mant).to(torch.uint8)

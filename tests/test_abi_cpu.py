@@ -121,3 +121,45 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         binding.reshape_and_cache(q, q, torch.zeros(4, 4, 16, 64), torch.zeros(4, 4, 16, 64),
                                   torch.zeros(2, dtype=torch.int64))
+
+
+def test_fp8_reshape_rejects(lib):
+    f = lib.pa_reshape_and_cache_fp8
+    ok = [A, A, A, A, A, 4, 8, 128, 16, 10, 1]
+    assert f(*ok, 0.0, 1.0, None) == INVALID                  # scale must be positive
+    assert f(*ok, 1.0, float("inf"), None) == INVALID
+    assert f(*ok, 1.0, float("nan"), None) == INVALID
+    bad = list(ok); bad[10] = 2                                # new rows as FP8: not supported
+    assert f(*bad, 1.0, 1.0, None) == UNSUPPORTED
+    bad = list(ok); bad[7] = 96
+    assert f(*bad, 1.0, 1.0, None) == UNSUPPORTED
+    bad = list(ok); bad[2] = A + 4                             # misaligned pool
+    assert f(*bad, 1.0, 1.0, None) == INVALID
+    assert f(0, 0, 0, 0, 0, 0, 8, 128, 16, 10, 1, 1.0, 1.0, None) == OK
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(out=A, query=A, kc=A, vc=A, bt=A, lens=A, S=4, Hq=8, Hkv=2, D=128, B=16, mbs=8,
+             NB=32, maxL=100, scale=0.1, ks=1.0, vs=1.0, ws=A2, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.pa_decode_fp8(a["out"], a["query"], a["kc"], a["vc"], a["bt"], a["lens"], a["S"],
+                             a["Hq"], a["Hkv"], a["D"], a["B"], a["mbs"], a["NB"], a["maxL"],
+                             a["scale"], a["ks"], a["vs"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ks=0.0), INVALID),
+    (dict(vs=-1.0), INVALID),
+    (dict(ks=float("nan")), INVALID),
+    (dict(S=8193), UNSUPPORTED),             # beyond the balanced split
+    (dict(Hq=32, Hkv=2), UNSUPPORTED),       # group 16 not built
+    (dict(D=96), UNSUPPORTED),
+    (dict(query=0), INVALID),
+    (dict(vc=A + 4), INVALID),
+    (dict(maxL=8 * 16 + 1), INVALID),
+    (dict(wsb=16), WORKSPACE),
+    (dict(ws=0), WORKSPACE),
+])
+def test_decode_fp8_rejects(lib, kw, status):
+    assert _decode_fp8(lib, **kw) == status
+    assert lib.pa_last_error().decode()
