@@ -65,6 +65,9 @@ def parse():
                          "pa_copy_blocks on the workload's pool")
     ap.add_argument("--copy-seqs", type=int, default=8,
                     help="sequences whose blocks a copy op moves")
+    ap.add_argument("--kv", default="native", choices=["native", "fp8"],
+                    help="native: pools in the workload's dtype (default); fp8: e4m3 pools "
+                         "written by pa_reshape_and_cache_fp8, decode by pa_decode_fp8")
     return ap.parse_args()
 
 
@@ -72,6 +75,7 @@ def parse():
 # profiles/hbm_traffic.txt are only reported while these are unchanged.
 KERNEL_SOURCES = {
     "decode_stream_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
+    "decode_stream_fp8_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
@@ -113,12 +117,38 @@ def fused_append(case) -> bool:
     return want == case.slot_mapping.tolist()
 
 
+# Per-pool scales of the FP8 benchmark pools: N(0, 1) data over 1/32 spans
+# +-14 before saturation.
+FP8_K_SCALE = FP8_V_SCALE = 1.0 / 32
+
+
+def fp8_pools_on_device(case, dev):
+    """FP8 pools (K [NB, Hkv, B, D], V [NB, Hkv, D, B] uint8) holding the
+    workload's pools, quantised by the library's own cache write: every slot
+    of the pool is written once."""
+    NB, Hkv, B, D = case.key_cache.shape
+    kc8 = torch.zeros((NB, Hkv, B, D), dtype=torch.uint8, device=dev)
+    vc8 = torch.zeros((NB, Hkv, D, B), dtype=torch.uint8, device=dev)
+    step = max(1, (1 << 28) // (2 * Hkv * B * D * case.key_cache.element_size()))
+    for b0 in range(0, NB, step):
+        b1 = min(NB, b0 + step)
+        rows_k = case.key_cache[b0:b1].permute(0, 2, 1, 3).reshape(-1, Hkv, D).to(dev)
+        rows_v = case.value_cache[b0:b1].permute(0, 2, 1, 3).reshape(-1, Hkv, D).to(dev)
+        slots = torch.arange(b0 * B, b1 * B, dtype=torch.int64, device=dev)
+        binding.reshape_and_cache_fp8(rows_k, rows_v, kc8, vc8, slots, FP8_K_SCALE, FP8_V_SCALE)
+    torch.cuda.synchronize()
+    return kc8, vc8
+
+
 class Replica:
     """One device copy of a workload."""
 
-    def __init__(self, case, dev):
-        self.kc = case.key_cache.to(dev)
-        self.vc = case.value_cache.to(dev)
+    def __init__(self, case, dev, fp8=False):
+        if fp8:
+            self.kc, self.vc = fp8_pools_on_device(case, dev)
+        else:
+            self.kc = case.key_cache.to(dev)
+            self.vc = case.value_cache.to(dev)
         self.q = case.query.to(dev)
         self.bt = case.block_tables.to(dev)
         self.lens = case.context_lens.to(dev)
@@ -126,7 +156,7 @@ class Replica:
         self.nv = case.new_value.to(dev)
         self.slots = case.slot_mapping.to(dev)
         self.out = torch.empty_like(self.q)
-        if fused_append(case):
+        if fused_append(case) and not fp8:
             S, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
             self.nk_seq = case.new_key.reshape(S, Hkv, D).to(dev)
             self.nv_seq = case.new_value.reshape(S, Hkv, D).to(dev)
@@ -157,13 +187,17 @@ def main():
         return run_copy(args, case, dev)
     S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
                         case.block_size)
-    eb = case.key_cache.element_size()
+    fp8 = args.kv == "fp8"
+    if fp8 and (case.dtype != "bf16" or case.num_chunks or args.partition_size):
+        print("--kv fp8 runs bf16 decode workloads with the balanced split", file=sys.stderr)
+        sys.exit(2)
+    eb = 1 if fp8 else case.key_cache.element_size()  # bytes per cached element
     lens = case.context_lens.tolist()
     maxL = case.max_context_len
     P = args.partition_size  # 0: balanced split of all units over the waves
-    reps = [Replica(case, dev)]
+    reps = [Replica(case, dev, fp8)]
     for _ in range(1, max(1, args.replicas)):
-        reps.append(Replica(case, dev))
+        reps.append(Replica(case, dev, fp8))
     ws = binding.make_workspace(reps[0].q, reps[0].kc, maxL, P)
     stream = torch.cuda.current_stream()
 
@@ -172,10 +206,11 @@ def main():
     if case.shared_blocks is not None:
         n_sh = case.shared_blocks.numel() * B
         unique = n_sh + sum(L - n_sh for L in lens)
-    dec_bytes = acct.decode_bytes(lens, Hq, Hkv, D, B, eb, unique_tokens=unique)
+    dec_bytes = acct.decode_bytes(lens, Hq, Hkv, D, B, eb, unique_tokens=unique,
+                                  q_elem_bytes=case.query.element_size())
     kv_bytes = (sum(lens) if unique is None else unique) * acct.kv_bytes_per_token(1, Hkv, D, eb)
     T = case.slot_mapping.numel()
-    cw_bytes = acct.cache_write_bytes(T, Hkv, D, eb)
+    cw_bytes = acct.cache_write_bytes(T, Hkv, D, eb, src_elem_bytes=case.new_key.element_size())
     chunks = []
     if case.num_chunks:
         cu = case.chunk_cu_query_lens.tolist()
@@ -186,18 +221,24 @@ def main():
 
     ev = {k: [] for k in ("cw0", "cw1", "dp0", "dp1", "dr1", "pf0", "pf1")}
 
-    fused = fused_append(case)
+    fused = fused_append(case) and not fp8
 
     def step(i, record):
         r = reps[i % len(reps)]
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw0"].append(e)
-        if T and not fused:
+        if T and fp8:
+            binding.reshape_and_cache_fp8(r.nk, r.nv, r.kc, r.vc, r.slots, FP8_K_SCALE,
+                                          FP8_V_SCALE, stream=stream)
+        elif T and not fused:
             binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw1"].append(e)
             ev["dp0"].append(e)
-        if fused:
+        if fp8:
+            binding.decode_fp8_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL,
+                                          FP8_K_SCALE, FP8_V_SCALE, ws, stream=stream)
+        elif fused:
             binding.decode_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
                                              r.lens, case.scale, maxL, P, ws, stream=stream)
         else:
@@ -262,7 +303,8 @@ def main():
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     # bf16 uses the matrix-core variant of the balanced split.
-    dp_kernel = ("decode_partition_kernel" if P != 0 or S > 8192 else
+    dp_kernel = ("decode_stream_fp8_kernel" if fp8 else
+                 "decode_partition_kernel" if P != 0 or S > 8192 else
                  "decode_stream_mma_kernel" if case.dtype == "bf16" else "decode_stream_kernel")
     # The fused step's decode kernel also moves the new tokens' rows.
     dp_bytes = dec_bytes + (cw_bytes if fused else 0)
@@ -278,14 +320,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype,
+        "dtype": "fp8_e4m3 kv, bf16 q" if fp8 else case.dtype,
         "data": "synthetic",
         "config": {
-            "workload": case.name,
+            "workload": case.name + (" (FP8 e4m3 KV cache)" if fp8 else ""),
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
             "cache_write": ("fused into the decode pass (pa_decode_append)" if fused
+                            else "pa_reshape_and_cache_fp8" if T and fp8
                             else "pa_reshape_and_cache" if T else "none"),
             "replicas": len(reps),
             "prefill_chunks": chunks,
@@ -320,7 +363,8 @@ def main():
                                  "GB/s": round(cw_bytes / (t_cw * 1e-3) / 1e9, 1)}
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, kv_bytes)
+        result["cpu_baseline"] = (cpu_baseline_fp8(case, reps[0], args.cpu_seconds, kv_bytes)
+                                  if fp8 else cpu_baseline(case, args.cpu_seconds, kv_bytes))
     print(json.dumps(result), flush=True)
 
 
@@ -511,6 +555,27 @@ def cpu_baseline(case, min_seconds, kv_bytes):
     return {"value": round(kv_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"full {case.name} decode (all {case.num_seqs} seqs x "
+                      f"{case.num_q_heads} q heads, fp64), {runs} runs, "
+                      f"{per * 1e3:.1f} ms per run"}
+
+
+def cpu_baseline_fp8(case, rep, min_seconds, kv_bytes):
+    """The fp64 oracle's decode over the same FP8 pools (copied to the host),
+    on this host's cores, repeated until min_seconds have passed."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    kc, vc = rep.kc.cpu(), rep.vc.cpu()
+    runs, t = 0, 0.0
+    while t < min_seconds or runs == 0:
+        t0 = time.perf_counter()
+        oracle.decode_fp8(case.query, kc, vc, case.block_tables, case.context_lens, case.scale,
+                          FP8_K_SCALE, FP8_V_SCALE)
+        t += time.perf_counter() - t0
+        runs += 1
+    per = t / runs
+    return {"value": round(kv_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full {case.name} decode over the FP8 pools (all {case.num_seqs} seqs x "
                       f"{case.num_q_heads} q heads, fp64), {runs} runs, "
                       f"{per * 1e3:.1f} ms per run"}
 

@@ -23,14 +23,16 @@ def _cdiv(a: int, b: int) -> int:
 
 def decode_bytes(context_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
                  head_dim: int, block_size: int, elem_bytes: int,
-                 unique_tokens: int | None = None) -> int:
+                 unique_tokens: int | None = None, q_elem_bytes: int | None = None) -> int:
     """K/V of every attended token (once per distinct physical token when
     ``unique_tokens`` is given, as for blocks shared by several sequences),
-    plus the query read and the output write, block-table entries and lengths."""
+    plus the query read and the output write, block-table entries and lengths.
+    ``elem_bytes`` is that of the cache (1 for FP8); the query and output use
+    ``q_elem_bytes`` (default: the same)."""
     S = len(context_lens)
     toks = sum(context_lens) if unique_tokens is None else unique_tokens
     kv = toks * kv_bytes_per_token(1, num_kv_heads, head_dim, elem_bytes)
-    qo = 2 * S * num_q_heads * head_dim * elem_bytes
+    qo = 2 * S * num_q_heads * head_dim * (q_elem_bytes or elem_bytes)
     bt = sum(_cdiv(L, block_size) for L in context_lens) * 4 + 4 * S
     return kv + qo + bt
 
@@ -39,9 +41,12 @@ def decode_flops(context_lens: Iterable[int], num_q_heads: int, head_dim: int) -
     return 4 * head_dim * num_q_heads * sum(context_lens)
 
 
-def cache_write_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
-    """Read K and V rows of the new tokens, write them into the pools, read slots."""
-    return num_tokens * num_kv_heads * head_dim * elem_bytes * 2 * 2 + 8 * num_tokens
+def cache_write_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, elem_bytes: int,
+                      src_elem_bytes: int | None = None) -> int:
+    """Read K and V rows of the new tokens (``src_elem_bytes`` each, default
+    ``elem_bytes``), write them into the pools (``elem_bytes`` each), read slots."""
+    n = num_tokens * num_kv_heads * head_dim * 2
+    return n * ((src_elem_bytes or elem_bytes) + elem_bytes) + 8 * num_tokens
 
 
 def prefill_flops(chunks: Iterable[tuple], num_q_heads: int, head_dim: int) -> int:

@@ -970,13 +970,20 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
 //
 // Layouts.  K: [block][kv head][token][dim], a unit of 16 tokens is 16 * D
 // contiguous bytes.  V: [block][kv head][dim][token] (each page transposed),
-// so the V^T operand of the P V product (dim x 4 consecutive tokens per lane)
-// is one 4-byte load per lane and tile, with no transpose through LDS.
+// so a unit's V is D rows of 16 bytes, one per dim, and the V^T operand of the
+// P V product (one dim x 4 consecutive tokens per lane) is one 4-byte word of
+// such a row.
 //   K operand, k-step ks: lane (l16, lg) holds token l16, dims lg * D/4 + 8 ks
-//     + [0, 8) -- one contiguous D/4-byte piece of the token's row per lane;
-//     the Q^T operand takes the same dims, so the contraction is unchanged.
+//     + [0, 8) -- one contiguous D/4-byte piece of the token's row per lane
+//     (16-byte loads); the Q^T operand takes the same dims, so the
+//     contraction is unchanged.
 //   V^T operand, tile dt: lane (l16, lg) holds dim dt * 16 + l16, tokens
-//     4 lg + [0, 4).
+//     4 lg + [0, 4).  The unit's rows go by DMA (16 bytes a lane, 1 KB an
+//     instruction) into a LDS slot of the wave, and come back as 4-byte LDS
+//     reads.  Loading the words straight from HBM would take D / 16 loads of
+//     256 bytes each per unit; the vector memory path keeps a bounded number
+//     of load instructions in flight, so the bytes in flight, and the rate,
+//     fall with the bytes per instruction.
 // K rows past the unit's valid tokens come back as zeros (buffer range); in V
 // they share a row with valid tokens, so a partial unit masks its bytes.
 // ---------------------------------------------------------------------------
@@ -986,6 +993,24 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
 #endif
 constexpr int kFp8Buffers = PA_FP8_BUFFERS;  // units in flight + 1 per wave
 constexpr int kFp8Waves = 4;                 // waves per workgroup
+
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
+    uint32_t r;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+// Completes the LDS reads above: their registers stay live until here.
+template <int N>
+__device__ __forceinline__ void lds_b32_wait(uint32_t (&v)[N]) {
+    static_assert(N == 4 || N == 8, "batch");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : : "memory");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                       "+v"(v[6]), "+v"(v[7])
+                     : : "memory");
+}
 
 // Two e4m3 codes (bytes 0-1, or 2-3 when HI) -> two bf16, exactly.
 template <bool HI>
@@ -1004,7 +1029,9 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
     constexpr int KS = D / 32, DT = D / 16, KB = D / 4, KW = KB / 16;
     constexpr int NB = kFp8Buffers;
     static_assert(G <= 16, "group fits the 16 columns");
+    constexpr int VSEG = D / 64;  // V DMA instructions per unit
     extern __shared__ int scan[];  // [S + 1], sized at launch
+    __shared__ __attribute__((aligned(1024))) char vslot[NW][NB][D * 16];
     scan_units<NW>(scan, context_lens, S, max_tokens);
     const int Hkv = num_kv_heads;
     const int64_t U = (int64_t)scan[S] * Hkv;
@@ -1023,7 +1050,8 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
     const char *kbase = (const char *)key_cache;
     const char *vbase = (const char *)value_cache;
     const int k_off = l16 * D + lg * KB;  // from the unit's first K row
-    const int v_off = l16 * B + lg * 4;   // from the unit's first token of dim 0
+    // V^T reads: row dt * 16 + l16 of the slot (16 bytes a row), word lg.
+    const uint32_t v_lane = (uint32_t)(l16 * 16 + lg * 4);
     const s16x4_mv ones_a = l16 == 0 ? s16x4_mv{0x3F80, 0x3F80, 0x3F80, 0x3F80} : s16x4_mv{0, 0, 0, 0};
 
     u32x4 qt[KS];
@@ -1098,7 +1126,6 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
         // Issue unit i of the chunk into buffer b.  Units past the segment get
         // empty ranges: no memory is touched and zeros land.
         u32x4 kb[NB][KW];
-        uint32_t vb[NB][DT];
         int nv[NB];
         auto issue = [&](int b, int i, int seg_end) __attribute__((always_inline)) {
             const int ii = i & 63;
@@ -1114,17 +1141,27 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
             const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(vbase + page + tokoff), (short)0, nvalid > 0 ? (D - 1) * B + kUnitTokens : 0,
                 0x00020000);
+            // V first: waiting for this unit's K registers then also covers
+            // its DMA (loads complete in issue order).
+#pragma unroll
+            for (int sg = 0; sg < VSEG; ++sg)
+                dma16_to_lds(rv, &vslot[w][b][sg * 1024], (sg * 64 + lane) * B);
 #pragma unroll
             for (int c = 0; c < KW; ++c)
                 kb[b][c] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + c * 16, 0, 0));
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                vb[b][dt] = __builtin_amdgcn_raw_buffer_load_b32(rv, v_off + dt * 16 * B, 0, 0);
         };
 
         auto process = [&](int b) __attribute__((always_inline)) {
             f32x4_mv st = {0.f, 0.f, 0.f, 0.f};
+            // This unit's loads are the oldest in flight: the NB - 1 younger
+            // units issued VSEG + KW loads each.  Once they are done, its V
+            // rows are in the slot.
+            asm volatile("s_waitcnt vmcnt(%0)" : : "n"((NB - 1) * (VSEG + KW)) : "memory");
+            const uint32_t vb0 = lds_offset(&vslot[w][b][0]) + v_lane;
+            uint32_t vw[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vw[dt] = lds_read_b32(vb0 + dt * 256);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const uint32_t w0 = kb[b][ks >> 1][(ks & 1) * 2];
@@ -1164,9 +1201,10 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
                 const int cnt = min(max(nv[b] - 4 * lg, 0), 4);
                 vmask = cnt == 4 ? 0xFFFFFFFFu : ((1u << (8 * cnt)) - 1u);
             }
+            lds_b32_wait<DT>(vw);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const uint32_t wv = vb[b][dt] & vmask;
+                const uint32_t wv = vw[dt] & vmask;
                 const s16x4_mv va = __builtin_bit_cast(
                     s16x4_mv, (uint64_t)e4m3x2_to_bf16x2<false>(wv) |
                                   ((uint64_t)e4m3x2_to_bf16x2<true>(wv) << 32));
