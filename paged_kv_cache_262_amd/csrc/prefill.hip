@@ -50,12 +50,19 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kPfWaves = 8;         // waves per workgroup: 2 key parities x 4 row groups
+#ifndef PA_PF_WAVES
+#define PA_PF_WAVES 8
+#endif
+constexpr int kPfWaves = PA_PF_WAVES;  // waves per workgroup: 2 key parities x row groups
 constexpr int kPfRows = 128;        // rows (query x head) per workgroup
 constexpr int kKeyBlock = 64;       // keys per LDS block
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
 constexpr float kPfRescale = 8.0f;  // log2 units
 constexpr int kBtCache = 2048;      // block-table entries a tile keeps in LDS
+#ifndef PA_PF_HALVES
+#define PA_PF_HALVES 2
+#endif
+constexpr int kPfHalves = PA_PF_HALVES;  // 32-key halves of a block per softmax pass (1 or 2)
 
 template <typename A, typename Bv>
 __device__ __forceinline__ floatx4_v mfma16x16x32(const A &a, const Bv &b, floatx4_v c) {
@@ -97,10 +104,13 @@ __device__ __forceinline__ s16x4 lds_read_tr16_off(uint32_t addr) {
     asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
     return r;
 }
-__device__ __forceinline__ void lds_wait(s16x4 (&v)[2][2][2]) {
+template <int A, int C>
+__device__ __forceinline__ void lds_wait(s16x4 (&v)[A][C][2]) {
+    static_assert(A * C == 4, "a batch of eight reads");
     asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
-                   "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1]));
+                 : "+v"(v[0 / C][0 % C][0]), "+v"(v[0 / C][0 % C][1]), "+v"(v[1 / C][1 % C][0]),
+                   "+v"(v[1 / C][1 % C][1]), "+v"(v[2 / C][2 % C][0]), "+v"(v[2 / C][2 % C][1]),
+                   "+v"(v[3 / C][3 % C][0]), "+v"(v[3 / C][3 % C][1]));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -304,108 +314,127 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
                                 ((LY::swz(v_row) ^ ((l16 & 3) >> 1)) << 4);
 
     // One 64-key block of this wave's parity: S^T = K Q^T, online softmax,
-    // O^T += V^T P^T.
+    // O^T += V^T P^T, in 64 / (32 NH) passes of NH 32-key halves (fewer
+    // passes: fewer rescale checks; more: a smaller live S / P^T state).
     // dma_stage != nullptr: issue this wave's share of the DMA of pair
-    // dma_pair after the softmax, before the P V products.
+    // dma_pair after the first pass's softmax, before its P V products.
+    constexpr int NH = kPfHalves;     // 32-key halves per pass
+    constexpr int NKT = 2 * NH;       // 16-key tiles per pass
+    constexpr int VB = 4 / NH;        // dim tiles per batch of transposing reads
+    static_assert(DT % VB == 0, "dim tiles split into batches");
     auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
                        uint64_t seg_phys) __attribute__((always_inline)) {
-        floatx4_v s[4][RT];
+        const uint32_t vbase = lds_addr(Vb) + v_lane_off;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            u32x4 kf[KS];
+        for (int hp = 0; hp < 2 / NH; ++hp) {
+            const int kt0 = hp * NKT;  // first 16-key tile of the pass
+            floatx4_v s[NKT][RT];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[ks] = *(const u32x4 *)(Kb + kt * 16 * ROWB + k_row_off +
-                                          (((ks * 4 + lg) ^ k_sw) << 4));
+            for (int kt = 0; kt < NKT; ++kt) {
+                u32x4 kf[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[ks] = *(const u32x4 *)(Kb + (kt0 + kt) * 16 * ROWB + k_row_off +
+                                              (((ks * 4 + lg) ^ k_sw) << 4));
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    floatx4_v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kf[ks], qf[rt][ks], a);
+                    s[kt][rt] = a;
+                }
+            }
+            // Causal mask: only passes that reach past the tile's first
+            // position need it (a uniform branch).  Masked logits are -inf,
+            // never scaled.
+            const int pkey0 = key0 + kt0 * 16;
+            if (pkey0 + NKT * 16 - 1 > pos0) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (pkey0 + kt * 16 + lg * 4 + i > row_pos[rt]) s[kt][rt][i] = NEG_INF;
+            }
+            u32x4 pf[RT][NH];  // P^T operands: [rt][32-key half of the pass]
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                floatx4_v a = {0.f, 0.f, 0.f, 0.f};
+                float mx = NEG_INF;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kf[ks], qf[rt][ks], a);
-                s[kt][rt] = a;
-            }
-        }
-        // Causal mask: only blocks that reach past the tile's first position
-        // need it (a uniform branch).  Masked logits are -inf, never scaled.
-        if (key0 + kKeyBlock - 1 > pos0) {
+                for (int kt = 0; kt < NKT; ++kt)
+                    mx = fmaxf(mx, fmaxf(fmaxf(s[kt][rt][0], s[kt][rt][1]),
+                                         fmaxf(s[kt][rt][2], s[kt][rt][3])));
+                mx = row_max4(mx);
+                // The reference maximum m_row (log2 units) is raised only
+                // when a logit exceeds it by more than kPfRescale, so the
+                // rescale of the accumulators is rare; weights stay below
+                // 2^kPfRescale.
+                const float cand = mx * scale_log2;
+                if (__builtin_amdgcn_ballot_w64(cand > m_row[rt] + kPfRescale)) {
+                    const float mn = fmaxf(m_row[rt], cand);
+                    const float alpha = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - mn);
+                    m_row[rt] = mn;
+                    acc_l[rt] *= alpha;
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+                    for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] *= alpha;
+                }
+                const float mneg = (m_row[rt] == NEG_INF) ? 0.f : -m_row[rt];
+                float p[NKT][4];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (key0 + kt * 16 + lg * 4 + i > row_pos[rt]) s[kt][rt][i] = NEG_INF;
-        }
-        u32x4 pf[RT][2];  // P^T operands: [rt][32-key half]
+                        p[kt][i] = fast_exp2(fmaf(s[kt][rt][i], scale_log2, mneg));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            float mx = NEG_INF;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-                mx = fmaxf(mx, fmaxf(fmaxf(s[kt][rt][0], s[kt][rt][1]),
-                                     fmaxf(s[kt][rt][2], s[kt][rt][3])));
-            mx = row_max4(mx);
-            // The reference maximum m_row (log2 units) is raised only when a
-            // logit exceeds it by more than kPfRescale, so the rescale of the
-            // accumulators is rare; weights stay below 2^kPfRescale.
-            const float cand = mx * scale_log2;
-            if (__builtin_amdgcn_ballot_w64(cand > m_row[rt] + kPfRescale)) {
-                const float mn = fmaxf(m_row[rt], cand);
-                const float alpha = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - mn);
-                m_row[rt] = mn;
-                acc_l[rt] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] *= alpha;
-            }
-            const float mneg = (m_row[rt] == NEG_INF) ? 0.f : -m_row[rt];
-            float p[4][4];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(fmaf(s[kt][rt][i], scale_log2, mneg));
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                pf[rt][h][0] = pack_bf16x2(p[2 * h][0], p[2 * h][1]);
-                pf[rt][h][1] = pack_bf16x2(p[2 * h][2], p[2 * h][3]);
-                pf[rt][h][2] = pack_bf16x2(p[2 * h + 1][0], p[2 * h + 1][1]);
-                pf[rt][h][3] = pack_bf16x2(p[2 * h + 1][2], p[2 * h + 1][3]);
-            }
-            // Row sums on the matrix core: a ones row against the same bf16
-            // P^T the output uses, so numerator and denominator agree.
-#pragma unroll
-            for (int h = 0; h < 2; ++h) acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
-        }
-        if (dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
-        // O^T += V^T P^T, two dim tiles per batch; the transposing reads of
-        // the next batch are in flight while the current one multiplies.
-        const uint32_t vbase = lds_addr(Vb) + v_lane_off;
-        s16x4 vb[2][2][2][2];  // [buffer][dim tile of the batch][key half][rows +0 / +16]
-        auto issue_v = [&](s16x4 (&dst)[2][2][2], int dt0) __attribute__((always_inline)) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t a = vbase ^ ((uint32_t)(dt0 + j) << 5);
-                dst[j][0][0] = lds_read_tr16(a);
-                dst[j][0][1] = lds_read_tr16_off<16 * ROWB>(a);
-                dst[j][1][0] = lds_read_tr16_off<32 * ROWB>(a);
-                dst[j][1][1] = lds_read_tr16_off<48 * ROWB>(a);
-            }
-        };
-        issue_v(vb[0], 0);
-#pragma unroll
-        for (int b = 0; b < DT / 2; ++b) {
-            lds_wait(vb[b & 1]);
-            if (b + 1 < DT / 2) issue_v(vb[(b + 1) & 1], 2 * (b + 1));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const s16x8 vf =
-                        __builtin_shufflevector(vb[b & 1][j][h][0], vb[b & 1][j][h][1], 0, 1, 2, 3,
-                                                4, 5, 6, 7);
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        acc_o[2 * b + j][rt] = mfma16x16x32(vf, pf[rt][h], acc_o[2 * b + j][rt]);
+                for (int h = 0; h < NH; ++h) {
+                    pf[rt][h][0] = pack_bf16x2(p[2 * h][0], p[2 * h][1]);
+                    pf[rt][h][1] = pack_bf16x2(p[2 * h][2], p[2 * h][3]);
+                    pf[rt][h][2] = pack_bf16x2(p[2 * h + 1][0], p[2 * h + 1][1]);
+                    pf[rt][h][3] = pack_bf16x2(p[2 * h + 1][2], p[2 * h + 1][3]);
                 }
+                // Row sums on the matrix core: a ones row against the same
+                // bf16 P^T the output uses, so numerator and denominator agree.
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
+            }
+            if (hp == 0 && dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
+            // O^T += V^T P^T over the pass's halves, VB dim tiles per batch;
+            // the transposing reads of the next batch are in flight while the
+            // current one multiplies.
+            s16x4 vb[2][VB][NH][2];  // [buffer][dim tile of the batch][half][rows +0 / +16]
+            auto issue_v = [&](s16x4 (&dst)[VB][NH][2], int dt0) __attribute__((always_inline)) {
+#pragma unroll
+                for (int j = 0; j < VB; ++j) {
+                    const uint32_t a = (vbase + (uint32_t)(hp * NH * 32 * ROWB)) ^
+                                       ((uint32_t)(dt0 + j) << 5);
+                    dst[j][0][0] = lds_read_tr16(a);
+                    dst[j][0][1] = lds_read_tr16_off<16 * ROWB>(a);
+                    if constexpr (NH == 2) {
+                        dst[j][NH - 1][0] = lds_read_tr16_off<32 * ROWB>(a);
+                        dst[j][NH - 1][1] = lds_read_tr16_off<48 * ROWB>(a);
+                    }
+                }
+            };
+            issue_v(vb[0], 0);
+#pragma unroll
+            for (int b = 0; b < DT / VB; ++b) {
+                lds_wait(vb[b & 1]);
+                if (b + 1 < DT / VB) issue_v(vb[(b + 1) & 1], VB * (b + 1));
+#pragma unroll
+                for (int j = 0; j < VB; ++j)
+#pragma unroll
+                    for (int h = 0; h < NH; ++h) {
+                        const s16x8 vf = __builtin_shufflevector(vb[b & 1][j][h][0],
+                                                                 vb[b & 1][j][h][1], 0, 1, 2, 3,
+                                                                 4, 5, 6, 7);
+#pragma unroll
+                        for (int rt = 0; rt < RT; ++rt)
+                            acc_o[VB * b + j][rt] =
+                                mfma16x16x32(vf, pf[rt][h], acc_o[VB * b + j][rt]);
+                    }
+            }
         }
     };
 
