@@ -345,7 +345,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dp_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dp_kernel, case.name),
+            "traffic": measured_traffic(dp_kernel, case.name + ("_fp8" if fp8 else "")),
             "algorithmic_bytes_per_launch": dp_bytes,
         },
     }
