@@ -60,9 +60,12 @@ def load(path: str | None = None):
                                                  f32, f32]
     lib.oracle_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
                                       f32, i32, f32, f32]
+    lib.oracle_prefill_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                       i64, f32, i32, f32, f32]
     for f in (lib.oracle_gather, lib.oracle_decode, lib.oracle_prefill,
               lib.oracle_reshape_and_cache, lib.oracle_copy_blocks, lib.oracle_fp8_encode,
-              lib.oracle_fp8_decode, lib.oracle_reshape_and_cache_fp8, lib.oracle_decode_fp8):
+              lib.oracle_fp8_decode, lib.oracle_reshape_and_cache_fp8, lib.oracle_decode_fp8,
+              lib.oracle_prefill_fp8):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -211,4 +214,23 @@ def decode_fp8(query, key_cache, value_cache, block_tables, context_lens, scale,
                                  _ptr(value_cache.contiguous()), _ptr(bt), _ptr(lens), S, Hq, Hkv,
                                  D, B, bt.shape[1], NB, ctypes.c_float(scale), _DT[q.dtype],
                                  ctypes.c_float(k_scale), ctypes.c_float(v_scale)))
+    return out
+
+
+def prefill_fp8(query, key_cache, value_cache, block_tables, cu_query_lens, context_lens, scale,
+                k_scale, v_scale, lib=None):
+    """fp64 causal prefill chunks over FP8 pools (K [NB, Hkv, B, D], V [NB, Hkv, D, B])."""
+    lib = lib or load()
+    T, Hq, D = query.shape
+    NB, Hkv, B, _ = key_cache.shape
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    q = query.contiguous()
+    bt = block_tables.to(torch.int32).contiguous()
+    cu = cu_query_lens.to(torch.int32).contiguous()
+    lens = context_lens.to(torch.int32).contiguous()
+    _check(lib.oracle_prefill_fp8(out.ctypes.data, _ptr(q), _ptr(key_cache.contiguous()),
+                                  _ptr(value_cache.contiguous()), _ptr(bt), _ptr(cu), _ptr(lens),
+                                  lens.numel(), Hq, Hkv, D, B, bt.shape[1], NB,
+                                  ctypes.c_float(scale), _DT[q.dtype], ctypes.c_float(k_scale),
+                                  ctypes.c_float(v_scale)))
     return out

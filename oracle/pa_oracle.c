@@ -570,3 +570,94 @@ int oracle_decode_fp8(double *out, const void *query, const unsigned char *key_c
     }
     return status;
 }
+
+/*
+ * One query row over FP8 pools: gather the first L keys of a table row, each
+ * element its code's value times the pool's scale (K [block][head][offset][d],
+ * V [block][head][d][offset]), then the same attention as attend_row.
+ */
+static int attend_paged_fp8(double *out, const void *q_base, size_t q_off, int q_dtype,
+                            const unsigned char *key_cache, const unsigned char *value_cache,
+                            const int32_t *bt_row, int L, int num_kv_heads, int kv_head,
+                            int block_size, int D, int64_t num_blocks, double scale,
+                            double k_scale, double v_scale)
+{
+    size_t n = (size_t)(L > 0 ? L : 1) * D;
+    double *K = malloc(n * sizeof(double));
+    double *V = malloc(n * sizeof(double));
+    double *x = malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+    double *q = malloc((size_t)D * sizeof(double));
+    int st = 0;
+    if (!K || !V || !x || !q) {
+        st = 5;
+        goto done;
+    }
+    for (int j = 0; j < L; ++j) {
+        int32_t phys = bt_row[j / block_size];
+        int off = j % block_size;
+        if (phys < 0 || phys >= num_blocks) {
+            st = 2;
+            goto done;
+        }
+        size_t page = ((size_t)phys * num_kv_heads + kv_head) * (size_t)block_size * D;
+        for (int d = 0; d < D; ++d) {
+            K[(size_t)j * D + d] = e4m3_value(key_cache[page + (size_t)off * D + d]) * k_scale;
+            V[(size_t)j * D + d] = e4m3_value(value_cache[page + (size_t)d * block_size + off]) * v_scale;
+        }
+    }
+    for (int i = 0; i < D; ++i)
+        q[i] = widen(q_base, q_off + i, q_dtype);
+    attend_row(out, q, K, V, L, D, scale, x, NULL);
+done:
+    free(K);
+    free(V);
+    free(x);
+    free(q);
+    return st;
+}
+
+/*
+ * Prefill chunks over FP8 pools: as oracle_prefill (query i of chunk c at
+ * position context_lens[c] - n_c + i sees keys 0 .. that position), with the
+ * keys and values decoded as in oracle_decode_fp8.
+ */
+int oracle_prefill_fp8(double *out, const void *query, const unsigned char *key_cache,
+                       const unsigned char *value_cache, const int32_t *block_tables,
+                       const int32_t *cu_query_lens, const int32_t *context_lens, int num_chunks,
+                       int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                       int max_blocks, int64_t num_blocks, float scale, int q_dtype,
+                       float k_scale, float v_scale)
+{
+    if (num_chunks < 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+        return 1;
+    for (int c = 0; c < num_chunks; ++c) {
+        int n = cu_query_lens[c + 1] - cu_query_lens[c];
+        if (n < 0 || n > context_lens[c] || context_lens[c] > max_blocks * block_size)
+            return 1;
+    }
+    int group = num_q_heads / num_kv_heads;
+    int total = cu_query_lens[num_chunks];
+    int status = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int t = 0; t < total; ++t) {
+        for (int h = 0; h < num_q_heads; ++h) {
+            int c = 0;
+            while (cu_query_lens[c + 1] <= t)
+                ++c;
+            int n = cu_query_lens[c + 1] - cu_query_lens[c];
+            int i = t - cu_query_lens[c];
+            int pos = context_lens[c] - n + i;
+            size_t row = (size_t)t * num_q_heads + h;
+            int st = attend_paged_fp8(out + row * head_dim, query, row * head_dim, q_dtype,
+                                      key_cache, value_cache, block_tables + (size_t)c * max_blocks,
+                                      pos + 1, num_kv_heads, h / group, block_size, head_dim,
+                                      num_blocks, (double)scale, (double)k_scale,
+                                      (double)v_scale);
+            if (st) {
+#pragma omp atomic write
+                status = st;
+            }
+        }
+    }
+    return status;
+}

@@ -552,6 +552,41 @@ def pin_fp8_decode_equals_dequantized_decode(lib):
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+def _fp8_prefill_case(lib, ks, vs):
+    c = W.random_case(72, "bf16", 2, 8, 2, 64, 16, 20, 60, write_new=False,
+                      chunks=[(37, 90), (16, 16), (5, 70)])
+    kc8 = oracle.fp8_encode(c.key_cache.float(), ks, lib=lib)
+    vc8 = oracle.fp8_encode(c.value_cache.float(), vs, lib=lib).permute(0, 1, 3, 2).contiguous()
+    return c, kc8, vc8
+
+
+def pin_fp8_prefill_equals_dequantized_prefill(lib):
+    """Prefill chunks over FP8 pools equal the plain prefill over float pools
+    that hold the dequantised values (exact in fp32 for these scales)."""
+    ks, vs = 0.25, 0.125
+    c, kc8, vc8 = _fp8_prefill_case(lib, ks, vs)
+    kf = torch.from_numpy(oracle.fp8_decode(kc8, lib=lib) * ks).float()
+    vf = torch.from_numpy(oracle.fp8_decode(vc8, lib=lib) * vs).float().permute(0, 1, 3, 2).contiguous()
+    ref = oracle.prefill(c.chunk_query.float(), kf, vf, c.chunk_block_tables,
+                         c.chunk_cu_query_lens, c.chunk_context_lens, c.scale, lib=lib)
+    out = oracle.prefill_fp8(c.chunk_query, kc8, vc8, c.chunk_block_tables, c.chunk_cu_query_lens,
+                             c.chunk_context_lens, c.scale, ks, vs, lib=lib)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_fp8_prefill_last_row_is_decode(lib):
+    """The last query of a chunk sees every key of its context: its row equals
+    FP8 decode over the same table and length."""
+    ks, vs = 0.03, 0.07
+    c, kc8, vc8 = _fp8_prefill_case(lib, ks, vs)
+    out = oracle.prefill_fp8(c.chunk_query, kc8, vc8, c.chunk_block_tables, c.chunk_cu_query_lens,
+                             c.chunk_context_lens, c.scale, ks, vs, lib=lib)
+    last = c.chunk_cu_query_lens[1:].long() - 1
+    dec = oracle.decode_fp8(c.chunk_query[last], kc8, vc8, c.chunk_block_tables,
+                            c.chunk_context_lens, c.scale, ks, vs, lib=lib)
+    np.testing.assert_allclose(out[last.numpy()], dec, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_gather_page_examples,
     pin_decode_one_hot_page_examples,
@@ -577,4 +612,6 @@ ALL_PINS = [
     pin_fp8_encode_rounding,
     pin_fp8_cache_write_layout,
     pin_fp8_decode_equals_dequantized_decode,
+    pin_fp8_prefill_equals_dequantized_prefill,
+    pin_fp8_prefill_last_row_is_decode,
 ]

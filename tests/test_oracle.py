@@ -60,6 +60,17 @@ MUTATIONS = {
     "fp8_v_not_transposed": ("value_cache[page + (size_t)d * block_size + off] =",
                              "value_cache[page + (size_t)off * head_dim + d] ="),
     "fp8_subnormal_exponent": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
+    "fp8_prefill_drops_diagonal": (
+        "                                      pos + 1, num_kv_heads, h / group, block_size, head_dim,\n"
+        "                                      num_blocks, (double)scale, (double)k_scale,",
+        "                                      pos, num_kv_heads, h / group, block_size, head_dim,\n"
+        "                                      num_blocks, (double)scale, (double)k_scale,"),
+    "fp8_prefill_v_untransposed": (
+        "e4m3_value(value_cache[page + (size_t)d * block_size + off]) * v_scale;",
+        "e4m3_value(value_cache[page + (size_t)off * D + d]) * v_scale;"),
+    "fp8_prefill_k_with_v_scale": (
+        "e4m3_value(key_cache[page + (size_t)off * D + d]) * k_scale;",
+        "e4m3_value(key_cache[page + (size_t)off * D + d]) * v_scale;"),
     "copy_v_from_k": ("memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_value + src,",
                       "memcpy(snap_v + (size_t)i * block_bytes, (const char *)src_key + src,"),
     "copy_wrong_source": ("size_t src = (size_t)mapping[2 * i] * (size_t)block_bytes;",
