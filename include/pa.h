@@ -338,6 +338,23 @@ pa_status pa_decode_fp8(void *out, const void *query, const void *key_cache,
                         float scale, float k_scale, float v_scale, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/*
+ * pa_prefill_chunk_fp8 -- pa_prefill_chunk over FP8 pools: the same causal
+ * chunks, with keys and values the decoded codes times k_scale and v_scale.
+ * query and out are bf16 [total_query_tokens][num_q_heads][head_dim]; both
+ * products run on the bf16 matrix cores (the codes widen to bf16 exactly).
+ * The chunk's own new keys and values must already be in the pools
+ * (pa_reshape_and_cache_fp8).  Other arguments, conventions and errors as
+ * pa_prefill_chunk; scales must be positive and finite.
+ */
+pa_status pa_prefill_chunk_fp8(void *out, const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *cu_query_lens, const int32_t *context_lens,
+                               int32_t num_chunks, int32_t max_query_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                               float k_scale, float v_scale, void *stream);
+
 pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key_cache,
                                    const void *value_cache, const int32_t *block_tables,
                                    const int32_t *context_lens, int32_t num_seqs,

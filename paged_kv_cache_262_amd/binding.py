@@ -50,6 +50,8 @@ SIGNATURES = {
                                         _i32, _f, _f, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                              _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
+    "pa_prefill_chunk_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _i64, _f, _f, _f, _vp]),
     "pa_decode_fp8_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
     "pa_bm_create": (_i32, [_i64, _i32, _i32, _vp]),
@@ -300,6 +302,23 @@ def decode_fp8_partitions(out, query, key_cache, value_cache, block_tables, cont
     _check(load().pa_decode_fp8_partitions(*_fp8_decode_args(
         out, query, key_cache, value_cache, block_tables, context_lens, max_context_len, scale,
         k_scale, v_scale, workspace), _stream(stream)))
+
+
+def prefill_chunk_fp8(out, query, key_cache, value_cache, block_tables, cu_query_lens,
+                      context_lens, scale, max_query_len, k_scale, v_scale, stream=None):
+    """Causal chunks [Tq, Hq, D] (bf16) against FP8 pools; writes bf16 ``out``."""
+    Tq, Hq, D = query.shape
+    NB, Hkv, B, _ = _fp8_pools(key_cache, value_cache)
+    if query.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("FP8 prefill takes a bf16 query and writes a bf16 output")
+    C = context_lens.numel()
+    _check(load().pa_prefill_chunk_fp8(
+        _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+        _dev(cu_query_lens, "cu_query_lens"), _dev(context_lens, "context_lens"), C,
+        int(max_query_len), Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
+        float(k_scale), float(v_scale), _stream(stream)))
+    return out
 
 
 def prefill_chunk(out, query, key_cache, value_cache, block_tables, cu_query_lens,

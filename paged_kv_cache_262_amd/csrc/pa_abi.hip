@@ -487,7 +487,60 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_blocks = num_blocks;
     a.scale = scale;
+    a.kv_fp8 = 0;
+    a.k_scale = 1.0f;
+    a.v_scale = 1.0f;
     return hip_status(pa::launch_prefill_chunk(a, (hipStream_t)stream), "prefill_chunk");
+}
+
+pa_status pa_prefill_chunk_fp8(void *out, const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *cu_query_lens, const int32_t *context_lens,
+                               int32_t num_chunks, int32_t max_query_len, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                               float k_scale, float v_scale, void *stream) {
+    pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, PA_BF16);
+    if (s != PA_OK) return s;
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+    if (num_chunks < 0 || num_chunks > 65535)
+        return fail(PA_ERR_INVALID_ARG, "num_chunks %d out of range", num_chunks);
+    if (max_query_len < 0) return fail(PA_ERR_INVALID_ARG, "max_query_len < 0");
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
+    if (num_chunks == 0 || max_query_len == 0) return PA_OK;
+    if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    CHECK_PTR(out, 16);
+    CHECK_PTR(query, 16);
+    CHECK_PTR(key_cache, 16);
+    CHECK_PTR(value_cache, 16);
+    CHECK_PTR(block_tables, 4);
+    CHECK_PTR(cu_query_lens, 4);
+    CHECK_PTR(context_lens, 4);
+    if (!pa::prefill_shape_supported(head_dim, block_size, num_q_heads / num_kv_heads))
+        return fail(PA_ERR_UNSUPPORTED, "prefill shape not supported");
+    pa::PrefillArgs a;
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.cu_query_lens = cu_query_lens;
+    a.context_lens = context_lens;
+    a.num_chunks = num_chunks;
+    a.max_query_len = max_query_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.scale = scale;
+    a.kv_fp8 = 1;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return hip_status(pa::launch_prefill_chunk(a, (hipStream_t)stream), "prefill_chunk_fp8");
 }
 
 pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,

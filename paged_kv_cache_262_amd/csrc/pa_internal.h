@@ -96,6 +96,10 @@ struct PrefillArgs {
         max_blocks_per_seq;
     int64_t num_blocks;
     float scale;
+    // Nonzero: e4m3 pools (K [NB][Hkv][B][D], V [NB][Hkv][D][B]) of value /
+    // k_scale and value / v_scale; query and output are bf16.
+    int kv_fp8;
+    float k_scale, v_scale;
 };
 
 hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream);

@@ -515,12 +515,402 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill chunk over an FP8 (e4m3) cache.
+//
+// The pools hold e4m3 codes of value / scale, one fp32 scale per pool
+// (quantised KV cache: "vLLM Guide: High-Throughput Multi-GPU LLM Serving
+// with PagedAttention", the quantisation support among the engine's pillars
+// and its FP8 engine example).  K is [block][kv head][token][dim]; V is
+// [block][kv head][dim][token], each page transposed.  Every code widens to
+// bf16 exactly, so the tiling, products, softmax and merge are those of
+// prefill_chunk_kernel; k_scale rides in the softmax scale and v_scale in the
+// final normalisation.
+//
+// Staging (half the bytes of bf16): a 64-key block of K is 64 rows of D bytes,
+// moved by DMA with the 16-byte chunks of a row XOR-permuted by the key; a
+// block of V is its 64 / B transposed pages, moved as they are (a page is D
+// rows of B bytes, one per dim).
+//
+// Key order.  Row r of 16-key tile kt of a block holds key
+// 32 (kt >> 1) + 8 (r >> 2) + (r & 3) + 4 (kt & 1): the S^T fragment a lane
+// gets from tiles 2h and 2h + 1 then covers 8 consecutive keys of 32-key half
+// h, so its P^T operand pairs with a V^T operand (one dim x 8 keys) that is a
+// single 8-byte read of a transposed page row.  The K operand is one D/4-byte
+// piece of a key's row per lane (dims lg * D/4 + 8 ks + [0, 8) in k-step ks),
+// and Q^T takes the same dims.  Keys past the tile's last key share their V
+// words with valid keys; in the tile's last block those bytes are zeroed
+// before widening (their weights are 0, their codes may be anything).
+// ---------------------------------------------------------------------------
+
+// Two e4m3 codes (bytes 0-1, or 2-3 when HI) -> two bf16, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Eight codes (two words, lowest byte first) -> eight bf16.
+__device__ __forceinline__ u32x4 e4m3x8_bf16x8(uint32_t w0, uint32_t w1) {
+    return u32x4{e4m3x2_bf16x2<false>(w0), e4m3x2_bf16x2<true>(w0), e4m3x2_bf16x2<false>(w1),
+                 e4m3x2_bf16x2<true>(w1)};
+}
+
+template <int D, int B>
+struct KvLds8 {
+    static constexpr int NCH = D / 16;                     // 16-byte chunks per K row
+    static constexpr int KPS = 1024 / D;                   // K rows per 1 KB DMA segment
+    static constexpr int BLOCK_BYTES = kKeyBlock * D;      // 64 keys of K, or of V
+    static constexpr int SEGS = BLOCK_BYTES / 1024;        // segments per block
+    static constexpr int STAGE_BYTES = 4 * BLOCK_BYTES;    // K even, K odd, V even, V odd
+    static constexpr int SEGS_PER_WAVE = 4 * SEGS / kPfWaves;
+    static constexpr int PAGE_BYTES = B * D;               // one transposed V page
+    static constexpr int SEGS_PER_PAGE = PAGE_BYTES / 1024;
+    static_assert(4 * SEGS % kPfWaves == 0, "segments split evenly over the waves");
+    static_assert(PAGE_BYTES % 1024 == 0 && B >= KPS, "pages are whole segments");
+    // Chunk position of chunk c of K row `key` (inside the block): c ^ swz(key).
+    // The 8 lanes of a K read take keys k0 + {0..3, 8..11}; swz maps them to
+    // distinct chunks, and with rows of 128 bytes to distinct banks.
+    static __host__ __device__ constexpr int swz(int key) {
+        return D == 128 ? ((key & 3) | ((key >> 1) & 4)) : ((key >> 3) & 1);
+    }
+    // The permutation of a K segment's rows depends only on its parity.
+    static constexpr bool parity_only() {
+        for (int s = 0; s < SEGS; ++s)
+            for (int r = 0; r < KPS; ++r)
+                if (swz(s * KPS + r) != swz((s & 1) * KPS + r)) return false;
+        return true;
+    }
+};
+
+template <int D, int B, int G>
+__global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
+    bf16_t *__restrict__ out, const bf16_t *__restrict__ query,
+    const uint8_t *__restrict__ key_cache, const uint8_t *__restrict__ value_cache,
+    const int32_t *__restrict__ block_tables, const int32_t *__restrict__ cu_query_lens,
+    const int32_t *__restrict__ context_lens, int num_q_heads, int num_kv_heads, int max_blocks,
+    int64_t num_blocks, float scale_log2, float v_scale, int num_tiles, int total) {
+    using LY = KvLds8<D, B>;
+    constexpr int QT = kPfRows / G;  // queries per tile
+    constexpr int KS = D / 32;       // k-steps of S^T = K Q^T
+    constexpr int DT = D / 16;       // 16-dim tiles of O^T
+    constexpr int KW = D / 64;       // 16-byte K reads per lane and key tile
+    constexpr int NRG = kPfWaves / 2;
+    constexpr int RT = kPfRows / (16 * NRG);
+    constexpr float NEG_INF = -__builtin_inff();
+    constexpr int MERGE_BYTES = NRG * 64 * DT * RT * 16;
+    constexpr int AREA = LY::STAGE_BYTES > MERGE_BYTES ? LY::STAGE_BYTES : MERGE_BYTES;
+    static_assert(kPfRows == NRG * RT * 16, "row groups x 2 key parities");
+    static_assert(LY::parity_only(), "segment lane offsets depend on parity only");
+
+    __shared__ __attribute__((aligned(1024))) char stage_a[AREA];
+    __shared__ __attribute__((aligned(1024))) char stage_b[AREA];
+    __shared__ int bt_s[kBtCache];
+
+    // Workgroup order as in prefill_chunk_kernel: the tiles of one (chunk, kv
+    // head) run on one XCD.
+    const int bid = blockIdx.x;
+    const int xcd = bid % kXcds, idx = bid / kXcds;
+    const int q8 = total / kXcds, rem = total % kXcds;
+    const int lin = xcd < rem ? xcd * (q8 + 1) + idx : rem * (q8 + 1) + (xcd - rem) * q8 + idx;
+    const int pair = lin / num_tiles, tile = lin - pair * num_tiles;
+    const int c = pair / num_kv_heads, g = pair - c * num_kv_heads;
+    const int q_begin = cu_query_lens[c];
+    const int n = cu_query_lens[c + 1] - q_begin;
+    const int q0 = tile * QT;
+    if (q0 >= n) return;
+    const int max_tokens = max_blocks * B;
+    int L = context_lens[c];
+    L = L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
+    const int nq = min(QT, n - q0);
+    const int pos0 = L - n + q0;
+    const int kend = min(L, pos0 + nq);
+    const int32_t *bt = block_tables + (int64_t)c * max_blocks;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int rg = w % NRG, kp = w / NRG;
+
+    // Rows and Q^T operands (dims lg * D/4 + 8 ks + [0, 8) in k-step ks).
+    int row_pos[RT];
+    bool row_ok[RT];
+    u32x4 qf[RT][KS];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = (rg * RT + rt) * 16 + l16;
+        const int qi = r / G, hh = r - qi * G;
+        row_ok[rt] = qi < nq;
+        const int qc = row_ok[rt] ? qi : nq - 1;
+        row_pos[rt] = pos0 + qc;
+        const bf16_t *qrow = query + ((int64_t)(q_begin + q0 + qc) * num_q_heads + g * G + hh) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[rt][ks] = *(const u32x4 *)(qrow + lg * (D / 4) + ks * 8);
+    }
+
+    floatx4_v acc_o[DT][RT];
+    floatx4_v acc_l[RT];
+    float m_row[RT];
+    const u32x4 ones_row = l16 == 0 ? u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}
+                                    : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m_row[rt] = NEG_INF;
+        acc_l[rt] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] = floatx4_v{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int64_t page_stride = (int64_t)B * D;  // bytes of one (block, kv head) page
+    const int nkb = cdiv(kend, kKeyBlock);
+    const int npairs = cdiv(nkb, 2);
+    const int nbt = cdiv(kend, B);
+
+    constexpr int kWinBlocks = kBtCache * B / kKeyBlock;
+    static_assert(kWinBlocks % 2 == 0, "windows hold whole pairs");
+    int win_kb0 = 0, win_p0 = 0;
+    auto load_window = [&](int kb0) __attribute__((always_inline)) {
+        win_kb0 = kb0;
+        win_p0 = kb0 * (kKeyBlock / B);
+        const int cnt = min(nbt - win_p0, kBtCache);
+        for (int i = tid; i < cnt; i += kPfWaves * 64) bt_s[i] = bt[win_p0 + i];
+    };
+    auto page_of = [&](int key) __attribute__((always_inline)) -> int64_t {
+        int phys = bt_s[key / B - win_p0];
+        if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;  // caller error: block 0
+        return ((int64_t)phys * num_kv_heads + g) * page_stride;
+    };
+
+    // DMA of one pair of blocks: 4 * SEGS segments of 1 KB ([K even][K odd]
+    // [V even][V odd]) split over the waves.  A K segment is KPS rows of one
+    // page; lane i moves chunk (i % NCH) ^ swz(row) of row i / NCH into LDS
+    // position i.  A V segment is 1 KB of one transposed page, moved as is.
+    // Pages past the tile's keys are replaced by the page of key kend - 1 (in
+    // V their bytes are zeroed before use), and in the tile's last block each
+    // K row past kend reads row kend - 1.
+    const int seg_row = lane / LY::NCH, seg_ch = lane % LY::NCH;
+    uint32_t seg_lane_off[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+        seg_lane_off[par] = (uint32_t)(seg_row * D + ((seg_ch ^ LY::swz(par * LY::KPS + seg_row)) << 4));
+    const char *kpool = (const char *)key_cache, *vpool = (const char *)value_cache;
+    auto lookup_pages = [&](int pr) __attribute__((always_inline)) -> uint64_t {
+        const int j = lane < LY::SEGS_PER_WAVE ? lane : 0;
+        const int seg = w * LY::SEGS_PER_WAVE + j;
+        const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1, s = seg % LY::SEGS;
+        const int kb = 2 * pr + bp;
+        if (tensor == 0) {
+            const int key_s = min(kb * kKeyBlock + s * LY::KPS, kend - 1);
+            return (uint64_t)(uintptr_t)(kpool + page_of(key_s) + (key_s % B) * D);
+        }
+        const int pg = s / LY::SEGS_PER_PAGE;
+        const int key_p = min(kb * kKeyBlock + pg * B, kend - 1);
+        return (uint64_t)(uintptr_t)(vpool + page_of(key_p) + (s % LY::SEGS_PER_PAGE) * 1024);
+    };
+    auto issue_dma = [&](char *stage, int pr, uint64_t seg_addr) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < LY::SEGS_PER_WAVE; ++j) {
+            const int seg = w * LY::SEGS_PER_WAVE + j;  // uniform
+            const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1;
+            const int s = seg % LY::SEGS;
+            const int kb = 2 * pr + bp;
+            if (kb >= nkb) continue;
+            lds_void *dst = (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024);
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)seg_addr, j);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(seg_addr >> 32), j);
+            const char *base = (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+            if (tensor == 1) {
+                __builtin_amdgcn_global_load_lds((const void *)(base + lane * 16), dst, 16, 0, 0);
+            } else if (kb * kKeyBlock + kKeyBlock <= kend) {
+                __builtin_amdgcn_global_load_lds((const void *)(base + seg_lane_off[s & 1]), dst, 16,
+                                                 0, 0);
+            } else {
+                const int kk = s * LY::KPS + seg_row;
+                const int key = min(kb * kKeyBlock + kk, kend - 1);
+                const char *src = kpool + page_of(key) + (key % B) * D +
+                                  ((seg_ch ^ LY::swz(kk)) << 4);
+                __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
+            }
+        }
+    };
+
+    // One 64-key block of this wave's parity.
+    auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
+                       uint64_t seg_phys) __attribute__((always_inline)) {
+        floatx4_v s[4][RT];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int key = (kt >> 1) * 32 + 8 * (l16 >> 2) + (l16 & 3) + 4 * (kt & 1);
+            u32x4 kraw[KW];
+#pragma unroll
+            for (int cc = 0; cc < KW; ++cc)
+                kraw[cc] = *(const u32x4 *)(Kb + key * D + (((lg * KW + cc) ^ LY::swz(key)) << 4));
+            u32x4 kf[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[ks] = e4m3x8_bf16x8(kraw[ks >> 1][(ks & 1) * 2], kraw[ks >> 1][(ks & 1) * 2 + 1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4_v a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kf[ks], qf[rt][ks], a);
+                s[kt][rt] = a;
+            }
+        }
+        // Causal mask (key of element i of tile kt: see the key order above).
+        if (key0 + kKeyBlock - 1 > pos0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (key0 + (kt >> 1) * 32 + 8 * lg + 4 * (kt & 1) + i > row_pos[rt])
+                            s[kt][rt][i] = NEG_INF;
+        }
+        u32x4 pf[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float mx = NEG_INF;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                mx = fmaxf(mx, fmaxf(fmaxf(s[kt][rt][0], s[kt][rt][1]),
+                                     fmaxf(s[kt][rt][2], s[kt][rt][3])));
+            mx = row_max4(mx);
+            const float cand = mx * scale_log2;
+            if (__builtin_amdgcn_ballot_w64(cand > m_row[rt] + kPfRescale)) {
+                const float mn = fmaxf(m_row[rt], cand);
+                const float alpha = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - mn);
+                m_row[rt] = mn;
+                acc_l[rt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] *= alpha;
+            }
+            const float mneg = (m_row[rt] == NEG_INF) ? 0.f : -m_row[rt];
+            float p[4][4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[kt][i] = fast_exp2(fmaf(s[kt][rt][i], scale_log2, mneg));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                pf[rt][h][0] = pack_bf16x2(p[2 * h][0], p[2 * h][1]);
+                pf[rt][h][1] = pack_bf16x2(p[2 * h][2], p[2 * h][3]);
+                pf[rt][h][2] = pack_bf16x2(p[2 * h + 1][0], p[2 * h + 1][1]);
+                pf[rt][h][3] = pack_bf16x2(p[2 * h + 1][2], p[2 * h + 1][3]);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
+        }
+        if (dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
+        // O^T += V^T P^T: dim dt * 16 + l16, keys 32 h + 8 lg + [0, 8).
+        const bool tail = key0 + kKeyBlock > kend;
+        uint32_t vmask[2][2];  // [half][word]: bytes of keys past kend are cleared
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k0 = key0 + 32 * h + 8 * lg;
+            const int cnt = tail ? min(max(kend - k0, 0), 8) : 8;
+            vmask[h][0] = cnt >= 4 ? 0xFFFFFFFFu : ((1u << (8 * cnt)) - 1u);
+            vmask[h][1] = cnt >= 8 ? 0xFFFFFFFFu : (cnt <= 4 ? 0u : ((1u << (8 * (cnt - 4))) - 1u));
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = dt * 16 + l16;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = 32 * h + 8 * lg;  // first key of the lane's 8, inside the block
+                const uint2 raw = *(const uint2 *)(Vb + (k / B) * LY::PAGE_BYTES + d * B + (k % B));
+                const u32x4 vf = e4m3x8_bf16x8(raw.x & vmask[h][0], raw.y & vmask[h][1]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc_o[dt][rt] = mfma16x16x32(vf, pf[rt][h], acc_o[dt][rt]);
+            }
+        }
+    };
+
+    auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
+        __syncthreads();
+        const bool next = pr + 1 < npairs;
+        uint64_t seg_phys = 0;
+        if (next) {
+            if (2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
+                load_window(2 * (pr + 1));
+                __syncthreads();
+            }
+            seg_phys = lookup_pages(pr + 1);
+        }
+        const bool works = 2 * pr + kp < nkb;
+        const bool late = next && works && kp == 1;
+        if (next && !late) issue_dma(nxt, pr + 1, seg_phys);
+        if (works)
+            compute(cur + kp * LY::BLOCK_BYTES, cur + (2 + kp) * LY::BLOCK_BYTES,
+                    (2 * pr + kp) * kKeyBlock, late ? nxt : nullptr, pr + 1, seg_phys);
+    };
+
+    load_window(0);
+    __syncthreads();
+    if (npairs > 0) issue_dma(stage_a, 0, lookup_pages(0));
+    for (int pr = 0; pr < npairs; pr += 2) {
+        step(stage_a, stage_b, pr);
+        if (pr + 1 < npairs) step(stage_b, stage_a, pr + 1);
+    }
+    __syncthreads();
+
+    // Merge the two key parities, normalise (times v_scale), store.
+    float *mo = (float *)stage_a + ((size_t)rg * 64 + lane) * (DT * RT * 4);
+    float *mml = (float *)stage_b + ((size_t)rg * 64 + lane) * (2 * RT);
+    float lsum[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) lsum[rt] = __shfl(acc_l[rt][0], l16);
+    if (kp == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) *(floatx4_v *)(mo + (rt * DT + dt) * 4) = acc_o[dt][rt];
+            mml[2 * rt] = m_row[rt];
+            mml[2 * rt + 1] = lsum[rt];
+        }
+    }
+    __syncthreads();
+    if (kp == 1) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const float m1 = mml[2 * rt], l1 = mml[2 * rt + 1];
+        const float M = fmaxf(m_row[rt], m1);
+        const float f0 = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - M);
+        const float f1 = (m1 == NEG_INF) ? 0.f : fast_exp2(m1 - M);
+        const float l = lsum[rt] * f0 + l1 * f1;
+        if (!row_ok[rt]) continue;
+        const float inv = l > 0.f ? v_scale / l : 0.f;
+        const int r = (rg * RT + rt) * 16 + l16;
+        const int qi = r / G, hh = r - qi * G;
+        bf16_t *orow = out + ((int64_t)(q_begin + q0 + qi) * num_q_heads + g * G + hh) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const floatx4_v o1 = *(const floatx4_v *)(mo + (rt * DT + dt) * 4);
+            const floatx4_v o = (acc_o[dt][rt] * f0 + o1 * f1) * inv;
+            uint2 v;
+            v.x = pack_bf16x2(o[0], o[1]);
+            v.y = pack_bf16x2(o[2], o[3]);
+            *(uint2 *)(orow + dt * 16 + lg * 4) = v;
+        }
+    }
+}
+
 template <int D, int B, int G>
 static hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
     constexpr int QT = kPfRows / G;
     const int tiles = cdiv(a.max_query_len, QT);
     const int64_t total = (int64_t)tiles * a.num_kv_heads * a.num_chunks;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
+    if (a.kv_fp8) {
+        hipLaunchKernelGGL((prefill_chunk_fp8_kernel<D, B, G>), dim3((unsigned)total),
+                           dim3(kPfWaves * 64), 0, stream, (bf16_t *)a.out,
+                           (const bf16_t *)a.query, (const uint8_t *)a.key_cache,
+                           (const uint8_t *)a.value_cache, a.block_tables, a.cu_query_lens,
+                           a.context_lens, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
+                           a.num_blocks, a.scale * kLog2e * a.k_scale, a.v_scale, tiles,
+                           (int)total);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((prefill_chunk_kernel<D, B, G>), dim3((unsigned)total), dim3(kPfWaves * 64),
                        0, stream, (bf16_t *)a.out, (const bf16_t *)a.query,
                        (const bf16_t *)a.key_cache, (const bf16_t *)a.value_cache, a.block_tables,

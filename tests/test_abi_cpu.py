@@ -163,3 +163,18 @@ def _decode_fp8(lib, **kw):
 def test_decode_fp8_rejects(lib, kw, status):
     assert _decode_fp8(lib, **kw) == status
     assert lib.pa_last_error().decode()
+
+
+def test_fp8_prefill_rejects(lib):
+    f = lib.pa_prefill_chunk_fp8
+    args = [A, A, A, A, A, A, A, 2, 512, 32, 8, 128, 16, 160, 1000, 0.1]
+    assert f(*args, 0.0, 1.0, None) == INVALID                     # scale must be positive
+    assert f(*args, 1.0, float("nan"), None) == INVALID
+    bad = list(args); bad[9] = 7                                    # 32 % 7
+    assert f(*bad, 1.0, 1.0, None) == INVALID
+    bad = list(args); bad[11] = 96
+    assert f(*bad, 1.0, 1.0, None) == UNSUPPORTED
+    bad = list(args); bad[3] = A + 4                                # misaligned V pool
+    assert f(*bad, 1.0, 1.0, None) == INVALID
+    bad = list(args); bad[7] = 0                                    # no chunks: nothing to do
+    assert f(*bad, 1.0, 1.0, None) == OK

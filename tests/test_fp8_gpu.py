@@ -202,3 +202,91 @@ def test_fp8_decode_llama8b_shape():
     out = gpu_decode_fp8(c, kc8, vc8, ks, vs)
     ref = oracle.decode_fp8(c.query, kc8, vc8, c.block_tables, c.context_lens, c.scale, ks, vs)
     check_close(out, ref, "bf16", "fp8 llama8b")
+
+
+# --------------------------------------------------------------- prefill -----
+
+def gpu_prefill_fp8(c, kc8, vc8, ks, vs):
+    q = dev(c.chunk_query)
+    out = torch.empty_like(q)
+    cu = c.chunk_cu_query_lens
+    maxq = int((cu[1:] - cu[:-1]).max())
+    binding.prefill_chunk_fp8(out, q, dev(kc8), dev(vc8), dev(c.chunk_block_tables), dev(cu),
+                              dev(c.chunk_context_lens), c.scale, maxq, ks, vs)
+    torch.cuda.synchronize()
+    return out
+
+
+def poison_chunk_tails(c, kc8, vc8):
+    """NaN codes past each chunk's context in its last page, and in every page
+    no chunk uses."""
+    B = c.block_size
+    used = set()
+    for k in range(c.num_chunks):
+        L = int(c.chunk_context_lens[k])
+        row = c.chunk_block_tables[k, :-(-L // B)].tolist()
+        used.update(row)
+        if L % B:
+            kc8[row[-1], :, L % B:, :] = NAN_CODE
+            vc8[row[-1], :, :, L % B:] = NAN_CODE
+    for s in range(c.num_seqs):
+        used.update(c.block_tables[s, :-(-int(c.context_lens[s]) // B)].tolist())
+    for blk in range(kc8.shape[0]):
+        if blk not in used:
+            kc8[blk] = NAN_CODE
+            vc8[blk] = NAN_CODE
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_fp8_prefill_parity_shapes(D, B, G):
+    """Ragged chunks (1 to 200 queries; contexts from one key to several tiles
+    of keys, ending inside a block) against the oracle, with NaN codes past
+    every context."""
+    chunks = [(7, 40), (130, 300), (64, 64), (1, 17), (200, 777)]
+    c = W.make_case("pf8", 27 + D + B + G, "bf16", 2 * G, 2, D, B, [5], new_positions=[4],
+                    chunks=chunks, extra_blocks=3)
+    ks, vs = 1.0 / 64, 1.0 / 32
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    poison_chunk_tails(c, kc8, vc8)
+    say("fp8 prefill shapes", D, B, G)
+    out = gpu_prefill_fp8(c, kc8, vc8, ks, vs)
+    ref = oracle.prefill_fp8(c.chunk_query, kc8, vc8, c.chunk_block_tables, c.chunk_cu_query_lens,
+                             c.chunk_context_lens, c.scale, ks, vs)
+    check_close(out, ref, "bf16", f"fp8 prefill D{D} B{B} G{G}")
+
+
+def test_fp8_prefill_mixed_workload():
+    """The mixed chunked-prefill shape (2 chunks of 512 queries over 2,048 prior
+    tokens, 32 q / 8 kv heads, d 128, B 16): the chunks' own tokens are written
+    by the FP8 cache write first, as a caller would, then prefill.  Every
+    output row of every 8th query is checked against the oracle; a prefill row
+    at position p is FP8 decode over the chunk's table with p + 1 keys (an
+    oracle identity pinned on the CPU)."""
+    c = W.mixed_chunked_prefill()
+    ks, vs = 0.05, 0.04
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 prefill mixed workload")
+    gk, gv = dev(kc8), dev(vc8)
+    binding.reshape_and_cache_fp8(dev(c.new_key), dev(c.new_value), gk, gv, dev(c.slot_mapping),
+                                  ks, vs)
+    q = dev(c.chunk_query)
+    out = torch.empty_like(q)
+    cu = c.chunk_cu_query_lens
+    binding.prefill_chunk_fp8(out, q, gk, gv, dev(c.chunk_block_tables), dev(cu),
+                              dev(c.chunk_context_lens), c.scale, 512, ks, vs)
+    torch.cuda.synchronize()
+    rk, rv = oracle.reshape_and_cache_fp8(c.new_key, c.new_value, kc8, vc8, c.slot_mapping, ks, vs)
+    assert torch.equal(gk.cpu(), rk) and torch.equal(gv.cpu(), rv)
+    rows, tables, lens = [], [], []
+    for k in range(c.num_chunks):
+        n = int(cu[k + 1] - cu[k])
+        L = int(c.chunk_context_lens[k])
+        for i in list(range(0, n, 8)) + [n - 1]:
+            rows.append(int(cu[k]) + i)
+            tables.append(c.chunk_block_tables[k])
+            lens.append(L - n + i + 1)
+    ref = oracle.decode_fp8(c.chunk_query[rows], rk, rv, torch.stack(tables),
+                            torch.tensor(lens, dtype=torch.int32), c.scale, ks, vs)
+    check_close(out[rows], ref, "bf16", "fp8 mixed prefill")
