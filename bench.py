@@ -79,6 +79,7 @@ KERNEL_SOURCES = {
     "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
+    "prefill_chunk_fp8_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
 }
 
 
@@ -156,7 +157,7 @@ class Replica:
         self.nv = case.new_value.to(dev)
         self.slots = case.slot_mapping.to(dev)
         self.out = torch.empty_like(self.q)
-        if fused_append(case) and not fp8:
+        if fused_append(case):
             S, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
             self.nk_seq = case.new_key.reshape(S, Hkv, D).to(dev)
             self.nv_seq = case.new_value.reshape(S, Hkv, D).to(dev)
@@ -188,8 +189,8 @@ def main():
     S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
                         case.block_size)
     fp8 = args.kv == "fp8"
-    if fp8 and (case.dtype != "bf16" or case.num_chunks or args.partition_size):
-        print("--kv fp8 runs bf16 decode workloads with the balanced split", file=sys.stderr)
+    if fp8 and (case.dtype != "bf16" or args.partition_size):
+        print("--kv fp8 runs bf16 workloads with the balanced split", file=sys.stderr)
         sys.exit(2)
     eb = 1 if fp8 else case.key_cache.element_size()  # bytes per cached element
     lens = case.context_lens.tolist()
@@ -221,13 +222,13 @@ def main():
 
     ev = {k: [] for k in ("cw0", "cw1", "dp0", "dp1", "dr1", "pf0", "pf1")}
 
-    fused = fused_append(case) and not fp8
+    fused = fused_append(case)
 
     def step(i, record):
         r = reps[i % len(reps)]
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw0"].append(e)
-        if T and fp8:
+        if T and fp8 and not fused:
             binding.reshape_and_cache_fp8(r.nk, r.nv, r.kc, r.vc, r.slots, FP8_K_SCALE,
                                           FP8_V_SCALE, stream=stream)
         elif T and not fused:
@@ -235,7 +236,11 @@ def main():
         if record:
             e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw1"].append(e)
             ev["dp0"].append(e)
-        if fp8:
+        if fp8 and fused:
+            binding.decode_fp8_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
+                                                 r.lens, case.scale, maxL, FP8_K_SCALE,
+                                                 FP8_V_SCALE, ws, stream=stream)
+        elif fp8:
             binding.decode_fp8_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL,
                                           FP8_K_SCALE, FP8_V_SCALE, ws, stream=stream)
         elif fused:
@@ -253,8 +258,13 @@ def main():
         if chunks:
             if record:
                 ev["pf0"].append(ev["dr1"][-1])
-            binding.prefill_chunk(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens, case.scale,
-                                  maxq, stream=stream)
+            if fp8:
+                binding.prefill_chunk_fp8(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens,
+                                          case.scale, maxq, FP8_K_SCALE, FP8_V_SCALE,
+                                          stream=stream)
+            else:
+                binding.prefill_chunk(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens, case.scale,
+                                      maxq, stream=stream)
             if record:
                 e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["pf1"].append(e)
 
@@ -327,7 +337,8 @@ def main():
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
-            "cache_write": ("fused into the decode pass (pa_decode_append)" if fused
+            "cache_write": ("fused into the decode pass (pa_decode_fp8_append)" if fused and fp8
+                            else "fused into the decode pass (pa_decode_append)" if fused
                             else "pa_reshape_and_cache_fp8" if T and fp8
                             else "pa_reshape_and_cache" if T else "none"),
             "replicas": len(reps),
@@ -351,12 +362,13 @@ def main():
     }
     if chunks:
         tf = pf_flops / (t_pf * 1e-3) / 1e12
-        result["prefill_roofline"] = {"kernel": "prefill_chunk_kernel", "bound": "mfma",
+        pf_kernel = "prefill_chunk_fp8_kernel" if fp8 else "prefill_chunk_kernel"
+        result["prefill_roofline"] = {"kernel": pf_kernel, "bound": "mfma",
                                       "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                       "unit": "TFLOP/s",
                                       "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                      "traffic": measured_traffic("prefill_chunk_kernel",
-                                                                  case.name),
+                                      "traffic": measured_traffic(
+                                          pf_kernel, case.name + ("_fp8" if fp8 else "")),
                                       "algorithmic_flops_per_launch": pf_flops}
     if T and not fused:
         result["cache_write"] = {"ms": round(t_cw, 5), "bytes": cw_bytes,

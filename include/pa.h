@@ -339,6 +339,34 @@ pa_status pa_decode_fp8(void *out, const void *query, const void *key_cache,
                         size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_fp8_append -- one FP8 decode step with its new tokens: the bf16
+ * rows new_key[s], new_value[s] ([num_seqs][num_kv_heads][head_dim]) are
+ * quantised into the slot of position context_lens[s] - 1 of sequence s
+ * (block block_tables[s][(L - 1) / block_size], offset (L - 1) % block_size),
+ * exactly as pa_reshape_and_cache_fp8 would, and the step attends over them:
+ * the pools and out equal pa_reshape_and_cache_fp8 followed by pa_decode_fp8,
+ * bit for bit.  The write happens inside the decode pass (no extra launch).
+ * Sequences with context_lens[s] == 0 or above max_context_len get no write.
+ * pa_decode_fp8_append_partitions is its first phase; pa_decode_reduce (as
+ * for pa_decode_fp8) completes it.  Other conventions as pa_decode_fp8.
+ */
+pa_status pa_decode_fp8_append(void *out, const void *query, const void *new_key,
+                               const void *new_value, void *key_cache, void *value_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, int32_t max_context_len, float scale,
+                               float k_scale, float v_scale, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+pa_status pa_decode_fp8_append_partitions(
+    void *out, const void *query, const void *new_key, const void *new_value, void *key_cache,
+    void *value_cache, const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len, float scale,
+    float k_scale, float v_scale, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pa_prefill_chunk_fp8 -- pa_prefill_chunk over FP8 pools: the same causal
  * chunks, with keys and values the decoded codes times k_scale and v_scale.
  * query and out are bf16 [total_query_tokens][num_q_heads][head_dim]; both

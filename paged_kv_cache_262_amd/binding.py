@@ -50,6 +50,11 @@ SIGNATURES = {
                                         _i32, _f, _f, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                              _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
+    "pa_decode_fp8_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
+    "pa_decode_fp8_append_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _i64, _i32, _f, _f,
+                                               _f, _vp, _sz, _vp]),
     "pa_prefill_chunk_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i32, _i64, _f, _f, _f, _vp]),
     "pa_decode_fp8_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
@@ -276,6 +281,38 @@ def _fp8_decode_args(out, query, key_cache, value_cache, block_tables, context_l
             _dev(context_lens, "context_lens"), S, Hq, Hkv, D, B, block_tables.shape[1], NB,
             int(max_context_len), float(scale), float(k_scale), float(v_scale),
             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size())
+
+
+def _fp8_append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                     context_lens, max_context_len, scale, k_scale, v_scale, workspace):
+    d = _fp8_decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                         max_context_len, scale, k_scale, v_scale, workspace)
+    S, Hkv, D = query.shape[0], key_cache.shape[1], query.shape[2]
+    for t, name in ((new_key, "new_key"), (new_value, "new_value")):
+        if tuple(t.shape) != (S, Hkv, D) or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be [{S}, {Hkv}, {D}] bfloat16")
+    return d[:2] + (_dev(new_key, "new_key"), _dev(new_value, "new_value")) + d[2:]
+
+
+def decode_fp8_append(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                      context_lens, scale, max_context_len, k_scale, v_scale, workspace=None,
+                      stream=None):
+    """One FP8 decode step with its new tokens: quantises new_key/new_value [S, Hkv, D] into
+    position context_lens[s] - 1 of each sequence and attends over it; writes ``out``."""
+    if workspace is None:
+        workspace = make_fp8_workspace(query, key_cache, max_context_len)
+    _check(load().pa_decode_fp8_append(*_fp8_append_args(
+        out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+        max_context_len, scale, k_scale, v_scale, workspace), _stream(stream)))
+    return out
+
+
+def decode_fp8_append_partitions(out, query, new_key, new_value, key_cache, value_cache,
+                                 block_tables, context_lens, scale, max_context_len, k_scale,
+                                 v_scale, workspace, stream=None):
+    _check(load().pa_decode_fp8_append_partitions(*_fp8_append_args(
+        out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+        max_context_len, scale, k_scale, v_scale, workspace), _stream(stream)))
 
 
 def make_fp8_workspace(query, key_cache, max_context_len):

@@ -1018,14 +1018,19 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-template <int D, int B, int G, int NW>
+// AP (append): the step's new token of sequence s (bf16 rows new_key[s],
+// new_value[s], [S][Hkv][D]) sits at position L_s - 1; the wave that streams
+// the unit holding it quantises the rows (codes of x * k_inv, x * v_inv, as
+// the FP8 cache write) into their slot before it loads the unit.
+template <int D, int B, int G, int NW, bool AP>
 __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
     bf16_t *__restrict__ out, const bf16_t *__restrict__ query,
-    const uint8_t *__restrict__ key_cache, const uint8_t *__restrict__ value_cache,
+    uint8_t *__restrict__ key_cache, uint8_t *__restrict__ value_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens, int S,
     int num_q_heads, int num_kv_heads, int max_blocks, int max_tokens, int64_t num_blocks, int nw,
     float scale_log2, float v_scale, float *__restrict__ rec_o, float *__restrict__ rec_ml,
-    int *__restrict__ ws_scan) {
+    int *__restrict__ ws_scan, const bf16_t *__restrict__ new_key,
+    const bf16_t *__restrict__ new_value, float k_inv, float v_inv) {
     constexpr int KS = D / 32, DT = D / 16, KB = D / 4, KW = KB / 16;
     constexpr int NB = kFp8Buffers;
     static_assert(G <= 16, "group fits the 16 columns");
@@ -1104,24 +1109,97 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
 
     for (int64_t base = ua; base < ub; base += 64) {
         const int n = (int)min((int64_t)64, ub - base);
-        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0;
-        if (lane < n) {
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1;
+        int l_s = 0, l_j = 0, l_us = 1;
+        if (lane < n) {  // from the LDS scan alone
             const int64_t u = base + lane;
-            const int s = seq_of_unit(scan, S, u, Hkv);
-            const int us = scan[s + 1] - scan[s];
-            const int rem = (int)(u - (int64_t)scan[s] * Hkv);
-            const int g = rem / us;
-            const int j = rem - g * us;
-            l_item = s * Hkv + g;
-            const int L = clamp_len(context_lens[s], max_tokens);
-            const int tok = j * kUnitTokens;
+            l_s = seq_of_unit(scan, S, u, Hkv);
+            l_us = scan[l_s + 1] - scan[l_s];
+            const int rem = (int)(u - (int64_t)scan[l_s] * Hkv);
+            const int g = rem / l_us;
+            l_j = rem - g * l_us;
+            l_item = l_s * Hkv + g;
+        }
+        // Append: the new rows of the pairs ending in this chunk, PE pairs per
+        // pass.  A group of D / 4 lanes takes one pair, D / 8 lanes on its K
+        // row and D / 8 on its V row, 8 elements a lane; the first pass's
+        // rows are fetched together with the descriptors.
+        constexpr int GL = D / 4, PE = 64 / GL;
+        const int grp = lane / GL, c8 = lane % GL;
+        const bool isv = c8 >= GL / 2;
+        const int e0 = (isv ? c8 - GL / 2 : c8) * 8;  // first element of the lane
+        uint64_t ends = 0;
+        int first = -1;
+        u32x4 first_row = {0, 0, 0, 0};
+        auto take_ends = [&]() __attribute__((always_inline)) -> int {
+            int mine = -1;
+#pragma unroll
+            for (int e = 0; e < PE; ++e) {
+                if (ends) {
+                    const int bit = (int)__builtin_ctzll(ends);
+                    ends &= ends - 1;
+                    if (grp == e) mine = bit;
+                }
+            }
+            return mine;
+        };
+        auto fetch_row = [&](int mine) __attribute__((always_inline)) -> u32x4 {
+            const int it = __shfl(l_item, mine < 0 ? 0 : mine);
+            if (mine < 0) return u32x4{0, 0, 0, 0};
+            return *(const u32x4 *)((isv ? new_value : new_key) + (int64_t)it * D + e0);
+        };
+        if (AP) {
+            ends = __builtin_amdgcn_ballot_w64(lane < n && l_j == l_us - 1);
+            first = take_ends();
+            first_row = fetch_row(first);
+        }
+        if (lane < n) {
+            const int Lraw = context_lens[l_s];
+            const int L = clamp_len(Lraw, max_tokens);
+            const int tok = l_j * kUnitTokens;
             l_nvalid = min(kUnitTokens, L - tok);
             l_tokoff = tok % B;
-            const int phys = block_tables[(int64_t)s * max_blocks + tok / B];
+            const int phys = block_tables[(int64_t)l_s * max_blocks + tok / B];
             if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
             l_phys = phys;
+            if (AP && Lraw == L && l_j == l_us - 1 && l_nvalid > 0) l_new = l_nvalid - 1;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
+        if (AP) {
+            // Quantise and store the rows of one pass (ends whose position
+            // turned out invalid store nothing).
+            auto put = [&](int mine, const u32x4 &row) __attribute__((always_inline)) {
+                const int src = mine < 0 ? 0 : mine;
+                const int it = __shfl(l_item, src), ph = __shfl(l_phys, src);
+                const int to = __shfl(l_tokoff, src), nr = __shfl(l_new, src);
+                if (mine >= 0 && nr >= 0) {
+                    const float inv = isv ? v_inv : k_inv;
+                    uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t word = row[e >> 1];
+                        const float x = (e & 1) ? bf16_hi(word) : bf16_lo(word);
+                        wd[e >> 2] |= e4m3_code(x * inv) << (8 * (e & 3));
+                    }
+                    const int64_t page = (int64_t)ph * block_bytes + (int64_t)(it % Hkv) * head_bytes;
+                    if (!isv) {
+                        *(uint2 *)(key_cache + page + (int64_t)(to + nr) * D + e0) =
+                            make_uint2(wd[0], wd[1]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            value_cache[page + (int64_t)(e0 + e) * B + to + nr] =
+                                (uint8_t)(wd[e >> 2] >> (8 * (e & 3)));
+                    }
+                }
+            };
+            put(first, first_row);
+            while (ends) {
+                const int mine = take_ends();
+                put(mine, fetch_row(mine));
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
 
         // Issue unit i of the chunk into buffer b.  Units past the segment get
         // empty ranges: no memory is touched and zeros land.
@@ -1514,16 +1592,25 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int B, int G>
-static hipError_t launch_stream_fp8(const DecodeArgs &a, hipStream_t stream) {
-    const dim3 grid(cdiv(a.stream_waves, kFp8Waves));
-    const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
-    hipLaunchKernelGGL((decode_stream_fp8_kernel<D, B, G, kFp8Waves>), grid, dim3(kFp8Waves * 64),
-                       dyn, stream, (bf16_t *)a.out, (const bf16_t *)a.query,
-                       (const uint8_t *)a.key_cache, (const uint8_t *)a.value_cache,
+template <int D, int B, int G, bool AP>
+static void launch_stream_fp8_as(const DecodeArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_stream_fp8_kernel<D, B, G, kFp8Waves, AP>),
+                       dim3(cdiv(a.stream_waves, kFp8Waves)), dim3(kFp8Waves * 64),
+                       (size_t)(a.num_seqs + 1) * sizeof(int), stream, (bf16_t *)a.out,
+                       (const bf16_t *)a.query, (uint8_t *)a.key_cache, (uint8_t *)a.value_cache,
                        a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
                        a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
-                       a.scale * kLog2e * a.k_scale, a.v_scale, a.ws_o, a.ws_ml, a.ws_scan);
+                       a.scale * kLog2e * a.k_scale, a.v_scale, a.ws_o, a.ws_ml, a.ws_scan,
+                       (const bf16_t *)a.new_key, (const bf16_t *)a.new_value, 1.0f / a.k_scale,
+                       1.0f / a.v_scale);
+}
+
+template <int D, int B, int G>
+static hipError_t launch_stream_fp8(const DecodeArgs &a, hipStream_t stream) {
+    if (a.new_key)
+        launch_stream_fp8_as<D, B, G, true>(a, stream);
+    else
+        launch_stream_fp8_as<D, B, G, false>(a, stream);
     return hipGetLastError();
 }
 
@@ -1531,7 +1618,7 @@ template <typename T, int D, int B, int G>
 static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
     if (a.kv_fp8) {  // bf16 query and output over e4m3 pools, balanced split only
         if constexpr (std::is_same<T, bf16_t>::value)
-            if (a.stream_waves > 0 && !a.new_key) return launch_stream_fp8<D, B, G>(a, stream);
+            if (a.stream_waves > 0) return launch_stream_fp8<D, B, G>(a, stream);
         return hipErrorNotSupported;
     }
     if (PA_DECODE_MMA && std::is_same<T, bf16_t>::value && a.stream_waves > 0)

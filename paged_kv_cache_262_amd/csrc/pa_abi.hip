@@ -425,6 +425,54 @@ pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key
                       "decode_fp8_partitions");
 }
 
+pa_status pa_decode_fp8_append_partitions(
+    void *out, const void *query, const void *new_key, const void *new_value, void *key_cache,
+    void *value_cache, const int32_t *block_tables, const int32_t *context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len, float scale,
+    float k_scale, float v_scale, void *workspace, size_t workspace_bytes, void *stream) {
+    if (num_seqs > pa::kStreamMaxSeqs)
+        return fail(PA_ERR_UNSUPPORTED, "FP8 decode handles up to %d sequences per call",
+                    pa::kStreamMaxSeqs);
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, query, key_cache, value_cache, block_tables,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, num_blocks, max_context_len, 0,
+                               scale, PA_BF16, workspace, workspace_bytes, true);
+    if (s != PA_OK) return s;
+    if (num_seqs > 0) {
+        CHECK_PTR(new_key, 16);
+        CHECK_PTR(new_value, 16);
+    }
+    st.a.kv_fp8 = 1;
+    st.a.k_scale = k_scale;
+    st.a.v_scale = v_scale;
+    st.a.new_key = new_key;
+    st.a.new_value = new_value;
+    return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
+                      "decode_fp8_append_partitions");
+}
+
+pa_status pa_decode_fp8_append(void *out, const void *query, const void *new_key,
+                               const void *new_value, void *key_cache, void *value_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, int32_t max_context_len, float scale,
+                               float k_scale, float v_scale, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    pa_status s = pa_decode_fp8_append_partitions(
+        out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+        max_context_len, scale, k_scale, v_scale, workspace, workspace_bytes, stream);
+    if (s != PA_OK) return s;
+    return pa_decode_reduce(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            block_size, max_blocks_per_seq, max_context_len, 0, PA_BF16,
+                            workspace, workspace_bytes, stream);
+}
+
 pa_status pa_decode_fp8(void *out, const void *query, const void *key_cache,
                         const void *value_cache, const int32_t *block_tables,
                         const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,

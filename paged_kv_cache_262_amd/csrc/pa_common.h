@@ -72,6 +72,31 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// ---- e4m3 (OCP 8-bit float: bias 7, 3 mantissa bits, no infinities,
+// S.1111.111 = NaN, largest finite 448, smallest subnormal 2^-9) --------------
+// e4m3 code of y: nearest value, ties to the even code, saturating at +-448,
+// NaN -> 0x7F.  Written from the format's definition (no hardware
+// conversion), so these rules hold whatever an instruction would do.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t u = __float_as_uint(y);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7Fu;  // NaN
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fminf(__uint_as_float(u & 0x7fffffffu), 448.0f);
+    uint32_t code;
+    if (a < 0.015625f) {
+        // below 2^-6: subnormal codes 0..7 step 2^-9 (8 rounds up to 2^-6)
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        // normal: keep 3 of fp32's 23 mantissa bits, round half to even; a
+        // carry moves into the exponent.  Rebias the exponent 127 -> 7.
+        uint32_t b = __float_as_uint(a);
+        b += 0x7FFFFu + ((b >> 20) & 1u);
+        code = (b >> 20) - (120u << 3);
+    }
+    return sign | code;
+}
+
+
 // log2(e): softmax runs in base 2, the scale carries the conversion.
 constexpr float kLog2e = 1.4426950408889634f;
 

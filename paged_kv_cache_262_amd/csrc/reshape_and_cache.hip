@@ -64,27 +64,6 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *ke
 // multiply by 1 / scale (computed on the host), then rounded to the nearest
 // e4m3 value, ties to the even code, saturating at +-448; NaN gives 0x7F.
 
-// e4m3 code of y, from the format's definition (no hardware conversion, so
-// the saturation and NaN rules above hold whatever the instruction does).
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const uint32_t u = __float_as_uint(y);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7Fu;  // NaN
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fminf(__uint_as_float(u & 0x7fffffffu), 448.0f);
-    uint32_t code;
-    if (a < 0.015625f) {
-        // below 2^-6: subnormal codes 0..7 step 2^-9 (8 rounds up to 2^-6)
-        code = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {
-        // normal: keep 3 of fp32's 23 mantissa bits, round half to even; a
-        // carry moves into the exponent.  Rebias the exponent 127 -> 7.
-        uint32_t b = __float_as_uint(a);
-        b += 0x7FFFFu + ((b >> 20) & 1u);
-        code = (b >> 20) - (120u << 3);
-    }
-    return sign | code;
-}
-
 template <typename T>
 __device__ __forceinline__ void load4(const T *p, float (&x)[4]) {
     if constexpr (sizeof(T) == 4) {

@@ -290,3 +290,139 @@ def test_fp8_prefill_mixed_workload():
     ref = oracle.decode_fp8(c.chunk_query[rows], rk, rv, torch.stack(tables),
                             torch.tensor(lens, dtype=torch.int32), c.scale, ks, vs)
     check_close(out[rows], ref, "bf16", "fp8 mixed prefill")
+
+
+# ------------------------------------------------------------- invariants ----
+
+def _gpu_fp8_decode_bt(c, kc8, vc8, bt, ks, vs):
+    q = dev(c.query)
+    out = torch.empty_like(q)
+    binding.decode_fp8(out, q, dev(kc8), dev(vc8), dev(bt), dev(c.context_lens), c.scale,
+                       int(c.context_lens.max()), ks, vs)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_fp8_block_relabelling_invariance():
+    """Moving every physical block and its table entries gives a bit-identical
+    FP8 decode: the arithmetic follows logical positions only."""
+    c = W.random_case(308, "bf16", 6, 32, 8, 128, 16, 300, 2000, write_new=False)
+    ks, vs = 0.03, 0.05
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 relabelling invariance")
+    a = _gpu_fp8_decode_bt(c, kc8, vc8, c.block_tables, ks, vs)
+    pi = torch.randperm(c.num_blocks, generator=torch.Generator().manual_seed(4))
+    k2 = torch.empty_like(kc8); k2[pi] = kc8
+    v2 = torch.empty_like(vc8); v2[pi] = vc8
+    b = _gpu_fp8_decode_bt(c, k2, v2, pi[c.block_tables.long()].to(torch.int32), ks, vs)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_fp8_shared_prefix_invariance():
+    """Prefix blocks shared by every table (reference count 12) give the same
+    bits as private copies of them, and match the oracle."""
+    c = W.prefix_sharing_decode(num_seqs=12)
+    ks, vs = 0.04, 0.04
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 shared prefix invariance")
+    a = _gpu_fp8_decode_bt(c, kc8, vc8, c.block_tables, ks, vs)
+    shared = c.shared_blocks.long()
+    n, NB, S = len(shared), c.num_blocks, c.num_seqs
+    k2 = torch.cat([kc8] + [kc8[shared]] * S)
+    v2 = torch.cat([vc8] + [vc8[shared]] * S)
+    bt = c.block_tables.clone()
+    for s in range(S):
+        bt[s, :n] = torch.arange(NB + s * n, NB + (s + 1) * n, dtype=torch.int32)
+    b = _gpu_fp8_decode_bt(c, k2, v2, bt, ks, vs)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.decode_fp8(c.query, kc8, vc8, c.block_tables, c.context_lens, c.scale, ks, vs)
+    check_close(a, ref, "bf16", "fp8 prefix vs oracle")
+
+
+def test_fp8_decode_deterministic():
+    c = W.llama8b_decode(num_seqs=16)
+    kc8 = W.random_fp8_codes(309, (c.num_blocks, 8, 16, 128))
+    vc8 = W.random_fp8_codes(310, (c.num_blocks, 8, 128, 16))
+    say("fp8 determinism")
+    a = _gpu_fp8_decode_bt(c, kc8, vc8, c.block_tables, 0.125, 0.25)
+    b = _gpu_fp8_decode_bt(c, kc8, vc8, c.block_tables, 0.125, 0.25)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------ decode with append (fused) --
+
+def _fp8_append_vs_oracle(c, ks, vs, kc8, vc8, split=False):
+    """Fused FP8 step on the GPU; the pools must equal the oracle's FP8 cache
+    write of each sequence's new token at L - 1, the output the oracle decode
+    over them.  Returns (out, gpu pools)."""
+    from tests.test_append_gpu import per_sequence_rows
+    nk, nv = per_sequence_rows(c)
+    gk, gv = dev(kc8), dev(vc8)
+    q = dev(c.query)
+    out = torch.empty_like(q)
+    maxL = max(1, int(c.context_lens.max()))
+    bt, lens = dev(c.block_tables), dev(c.context_lens)
+    if split:
+        ws = binding.make_fp8_workspace(q, gk, maxL)
+        binding.decode_fp8_append_partitions(out, q, dev(nk), dev(nv), gk, gv, bt, lens, c.scale,
+                                             maxL, ks, vs, ws)
+        binding.decode_reduce(out, lens, c.num_kv_heads, c.block_size, c.block_tables.shape[1],
+                              maxL, 0, ws)
+    else:
+        binding.decode_fp8_append(out, q, dev(nk), dev(nv), gk, gv, bt, lens, c.scale, maxL, ks,
+                                  vs)
+    torch.cuda.synchronize()
+    rk, rv = oracle.reshape_and_cache_fp8(c.new_key, c.new_value, kc8, vc8, c.slot_mapping, ks, vs)
+    assert torch.equal(gk.cpu(), rk), "K pool"
+    assert torch.equal(gv.cpu(), rv), "V pool"
+    ref = oracle.decode_fp8(c.query, rk, rv, c.block_tables, c.context_lens, c.scale, ks, vs)
+    check_close(out, ref, "bf16", "fp8 append")
+    return out
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_fp8_append_parity_shapes(D, B, G):
+    Hkv = 2
+    gen = torch.Generator().manual_seed(3000 + D + B + G)
+    lens = [0, 1, B - 1, B, B + 1, 16, 17, 64, 65, 257, 700] + \
+        [int(x) for x in torch.randint(1, 1100, (3,), generator=gen)]
+    c = W.make_case("fp8 append", 12, "bf16", Hkv * G, Hkv, D, B, lens,
+                    new_positions=[L - 1 if L else None for L in lens], extra_blocks=2)
+    ks, vs = 1.0 / 64, 0.021
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 append shapes", D, B, G)
+    out = _fp8_append_vs_oracle(c, ks, vs, kc8, vc8)
+    assert (out[0] == 0).all()                      # empty context: zeros, nothing written
+
+
+def test_fp8_append_many_short_sequences():
+    """Hundreds of 1..40-token sequences: several new rows per 64-unit chunk."""
+    c = W.random_case(311, "bf16", 300, 8, 2, 128, 16, 1, 40, extra_blocks=5)
+    ks, vs = 0.05, 0.05
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 append short sequences")
+    _fp8_append_vs_oracle(c, ks, vs, kc8, vc8)
+
+
+def test_fp8_append_llama8b_matches_unfused_bitwise():
+    """The Llama-3-8B-shaped FP8 step: the fused step (one call, and its two
+    phases) equals pa_reshape_and_cache_fp8 + pa_decode_fp8 bit for bit."""
+    c = W.llama8b_decode()
+    kc8 = W.random_fp8_codes(312, (c.num_blocks, 8, 16, 128))
+    vc8 = W.random_fp8_codes(313, (c.num_blocks, 8, 128, 16))
+    ks, vs = 1.0 / 8, 1.0 / 4
+    say("fp8 append llama8b")
+    fused = _fp8_append_vs_oracle(c, ks, vs, kc8, vc8)
+    split = _fp8_append_vs_oracle(c, ks, vs, kc8, vc8, split=True)
+    gk, gv = dev(kc8), dev(vc8)
+    binding.reshape_and_cache_fp8(dev(c.new_key), dev(c.new_value), gk, gv, dev(c.slot_mapping),
+                                  ks, vs)
+    q = dev(c.query)
+    ref = torch.empty_like(q)
+    binding.decode_fp8(ref, q, gk, gv, dev(c.block_tables), dev(c.context_lens), c.scale,
+                       int(c.context_lens.max()), ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(split.view(torch.int16), ref.view(torch.int16))
