@@ -426,3 +426,25 @@ def test_fp8_append_llama8b_matches_unfused_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), ref.view(torch.int16))
     assert torch.equal(split.view(torch.int16), ref.view(torch.int16))
+
+
+def test_fp8_encoder_every_bf16_pattern():
+    """All 65,536 bf16 bit patterns (NaNs, infinities, subnormals, both zeros)
+    written through the FP8 cache write: every code equals the oracle's, at a
+    power-of-two scale (x / scale exact) and at a general one."""
+    T, Hkv, D, B = 64, 8, 128, 16
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    rows = bits.view(torch.bfloat16).reshape(T, Hkv, D)
+    rows_v = rows.flip(0).contiguous()               # V gets the patterns in another order
+    NB = T // B
+    slots = torch.arange(T, dtype=torch.int64)
+    for ks, vs in ((1.0, 0.25), (0.0371, 3.3)):
+        kc8 = torch.full((NB, Hkv, B, D), 0x55, dtype=torch.uint8)
+        vc8 = torch.full((NB, Hkv, D, B), 0x55, dtype=torch.uint8)
+        say("fp8 encoder, every bf16 pattern, scales", ks, vs)
+        gk, gv = dev(kc8), dev(vc8)
+        binding.reshape_and_cache_fp8(dev(rows), dev(rows_v), gk, gv, dev(slots), ks, vs)
+        torch.cuda.synchronize()
+        rk, rv = oracle.reshape_and_cache_fp8(rows, rows_v, kc8, vc8, slots, ks, vs)
+        assert torch.equal(gk.cpu(), rk), "K codes differ"
+        assert torch.equal(gv.cpu(), rv), "V codes differ"
