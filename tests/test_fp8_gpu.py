@@ -448,3 +448,27 @@ def test_fp8_encoder_every_bf16_pattern():
         rk, rv = oracle.reshape_and_cache_fp8(rows, rows_v, kc8, vc8, slots, ks, vs)
         assert torch.equal(gk.cpu(), rk), "K codes differ"
         assert torch.equal(gv.cpu(), rv), "V codes differ"
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("bf16", 32), ("f32", 16), ("f32", 32)])
+def test_fp8_cache_write_runs_of_consecutive_slots(dtype, B):
+    """A chunk's 300 new tokens at consecutive positions starting inside a
+    block (groups of 16 that lie in one block take whole-row V stores, the
+    others per-token writes), with a padding token and a foreign slot in the
+    middle: bit-exact against the oracle."""
+    c = W.make_case("fp8 runs", 314, dtype, 8, 4, 128, B, [1], chunks=[(300, 313)],
+                    extra_blocks=2)
+    slots = c.slot_mapping.clone()
+    slots = slots[-300:].clone()                      # the chunk's own positions 13 .. 312
+    nk, nv = c.new_key[-300:].contiguous(), c.new_value[-300:].contiguous()
+    slots[100] = -1                                   # padding
+    slots[200] = int(c.block_tables[0, 0]) * B        # the decode sequence's slot
+    ks, vs = 0.05, 1.0 / 16
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 cache write runs", dtype, B)
+    gk, gv = dev(kc8), dev(vc8)
+    binding.reshape_and_cache_fp8(dev(nk), dev(nv), gk, gv, dev(slots), ks, vs)
+    torch.cuda.synchronize()
+    rk, rv = oracle.reshape_and_cache_fp8(nk, nv, kc8, vc8, slots, ks, vs)
+    assert torch.equal(gk.cpu(), rk), "K pool differs"
+    assert torch.equal(gv.cpu(), rv), "V pool differs"
