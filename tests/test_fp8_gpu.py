@@ -472,3 +472,76 @@ def test_fp8_cache_write_runs_of_consecutive_slots(dtype, B):
     rk, rv = oracle.reshape_and_cache_fp8(nk, nv, kc8, vc8, slots, ks, vs)
     assert torch.equal(gk.cpu(), rk), "K pool differs"
     assert torch.equal(gv.cpu(), rv), "V pool differs"
+
+
+def test_fp8_block_manager_drives_decode():
+    """The host block manager drives FP8 decode steps: prompts sharing a system
+    prefix (reused through the prefix cache), a fork whose first write copies
+    the shared partial block (pa_copy_blocks on the FP8 pools), and each step's
+    new tokens quantised inside the decode pass (pa_decode_fp8_append).  Every
+    step's output must match the oracle over each sequence's logical rows."""
+    import random
+    from tests.test_block_manager_gpu import B as BB, D as DD, Hkv as HK, Hq as HQ, NB as NBB, kv_rows
+    ks, vs = 0.03, 0.03
+    rnd = random.Random(6)
+    bm = binding.BlockManager(NBB, BB, prefix_cache=True)
+    kc = torch.zeros((NBB, HK, BB, DD), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros((NBB, HK, DD, BB), dtype=torch.uint8, device="cuda")
+    tokens = {}
+    system = [rnd.randint(0, 50) for _ in range(2 * BB + 3)]
+    for s in range(3):
+        prompt = system + [rnd.randint(0, 50) for _ in range(rnd.randint(0, 30))]
+        slots, cached = bm.add_sequence(s, prompt)
+        tokens[s] = prompt
+        keep = [(sl, kv_rows(prompt[:t + 1])) for t, sl in enumerate(slots) if sl >= 0]
+        if keep:
+            k = torch.stack([r[0] for _, r in keep]).cuda()
+            v = torch.stack([r[1] for _, r in keep]).cuda()
+            binding.reshape_and_cache_fp8(k, v, kc, vc,
+                                          torch.tensor([a for a, _ in keep], dtype=torch.int64).cuda(),
+                                          ks, vs)
+    for step in range(4):
+        if step == 1:
+            bm.fork(0, 3)
+            tokens[3] = list(tokens[0])
+        seqs = sorted(tokens)
+        rows = []
+        for s in seqs:
+            tok = rnd.randint(0, 50)
+            tokens[s].append(tok)
+            bm.append(s, tok)            # the slot is the table's position L - 1
+            rows.append(kv_rows(tokens[s]))
+        copies = bm.take_copies()
+        if copies:
+            binding.copy_blocks(kc, vc, kc, vc, torch.tensor(copies, dtype=torch.int64).cuda())
+        tabs = [bm.block_table(s) for s in seqs]
+        width = max(len(t) for t, _ in tabs)
+        bt = torch.zeros((len(seqs), width), dtype=torch.int32)
+        for i, (t, _) in enumerate(tabs):
+            bt[i, :len(t)] = torch.tensor(t, dtype=torch.int32)
+        lens = torch.tensor([L for _, L in tabs], dtype=torch.int32)
+        nk = torch.stack([r[0] for r in rows]).cuda()
+        nv = torch.stack([r[1] for r in rows]).cuda()
+        q = torch.randn((len(seqs), HQ, DD)).to(torch.bfloat16)
+        out = torch.empty((len(seqs), HQ, DD), dtype=torch.bfloat16, device="cuda")
+        say("fp8 block manager step", step, "copies", len(copies))
+        binding.decode_fp8_append(out, q.cuda(), nk, nv, kc, vc, bt.cuda(), lens.cuda(), DD ** -0.5,
+                                  int(lens.max()), ks, vs)
+        torch.cuda.synchronize()
+        # reference: each sequence's logical rows, encoded by the oracle, laid out contiguously
+        maxL = int(lens.max())
+        nbl = -(-maxL // BB)
+        rk = torch.zeros((len(seqs) * nbl, HK, BB, DD), dtype=torch.bfloat16)
+        rv = torch.zeros_like(rk)
+        rbt = torch.zeros((len(seqs), nbl), dtype=torch.int32)
+        for i, s in enumerate(seqs):
+            for t in range(len(tokens[s])):
+                k, v = kv_rows(tokens[s][:t + 1])
+                rk[i * nbl + t // BB, :, t % BB] = k
+                rv[i * nbl + t // BB, :, t % BB] = v
+            rbt[i] = torch.arange(i * nbl, (i + 1) * nbl, dtype=torch.int32)
+        rk8 = oracle.fp8_encode(rk.float(), ks)
+        rv8 = oracle.fp8_encode(rv.float(), vs).permute(0, 1, 3, 2).contiguous()
+        ref = oracle.decode_fp8(q, rk8, rv8, rbt, lens, DD ** -0.5, ks, vs)
+        check_close(out, ref, "bf16", f"fp8 block manager step {step}")
+    bm.close()
