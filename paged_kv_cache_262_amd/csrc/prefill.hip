@@ -475,8 +475,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     // Each lane of an odd wave hands its (max, sum, O^T fragment) to the lane
     // of the even wave with the same rows; both use the same lane layout.
     static_assert(NRG * 64 * DT * RT * 4 * 4 <= LY::STAGE_BYTES, "merge area");
-    float *mo = (float *)stage_a + ((size_t)rg * 64 + lane) * (DT * RT * 4);
-    float *mml = (float *)stage_b + ((size_t)rg * 64 + lane) * (2 * RT);
+    // Lane-contiguous: fragment f of a row group's lanes is 64 consecutive
+    // 16-byte pieces, so the stores and loads below are free of bank conflicts.
+    float *mo = (float *)stage_a + (size_t)rg * 64 * (DT * RT * 4) + lane * 4;
+    float *mml = (float *)stage_b + (size_t)rg * 64 * (2 * RT) + lane;
     float lsum[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) lsum[rt] = __shfl(acc_l[rt][0], l16);  // row l16's sum
@@ -484,16 +486,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) *(floatx4_v *)(mo + (rt * DT + dt) * 4) = acc_o[dt][rt];
-            mml[2 * rt] = m_row[rt];
-            mml[2 * rt + 1] = lsum[rt];
+            for (int dt = 0; dt < DT; ++dt) *(floatx4_v *)(mo + (rt * DT + dt) * 256) = acc_o[dt][rt];
+            mml[(2 * rt) * 64] = m_row[rt];
+            mml[(2 * rt + 1) * 64] = lsum[rt];
         }
     }
     __syncthreads();
     if (kp == 1) return;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const float m1 = mml[2 * rt], l1 = mml[2 * rt + 1];
+        const float m1 = mml[(2 * rt) * 64], l1 = mml[(2 * rt + 1) * 64];
         const float M = fmaxf(m_row[rt], m1);
         const float f0 = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - M);
         const float f1 = (m1 == NEG_INF) ? 0.f : fast_exp2(m1 - M);
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
         bf16_t *orow = out + ((int64_t)(q_begin + q0 + qi) * num_q_heads + g * G + hh) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const floatx4_v o1 = *(const floatx4_v *)(mo + (rt * DT + dt) * 4);
+            const floatx4_v o1 = *(const floatx4_v *)(mo + (rt * DT + dt) * 256);
             const floatx4_v o = (acc_o[dt][rt] * f0 + o1 * f1) * inv;
             uint2 v;
             v.x = pack_bf16x2(o[0], o[1]);
@@ -855,8 +857,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
     __syncthreads();
 
     // Merge the two key parities, normalise (times v_scale), store.
-    float *mo = (float *)stage_a + ((size_t)rg * 64 + lane) * (DT * RT * 4);
-    float *mml = (float *)stage_b + ((size_t)rg * 64 + lane) * (2 * RT);
+    // Lane-contiguous: fragment f of a row group's lanes is 64 consecutive
+    // 16-byte pieces, so the stores and loads below are free of bank conflicts.
+    float *mo = (float *)stage_a + (size_t)rg * 64 * (DT * RT * 4) + lane * 4;
+    float *mml = (float *)stage_b + (size_t)rg * 64 * (2 * RT) + lane;
     float lsum[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) lsum[rt] = __shfl(acc_l[rt][0], l16);
@@ -864,16 +868,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) *(floatx4_v *)(mo + (rt * DT + dt) * 4) = acc_o[dt][rt];
-            mml[2 * rt] = m_row[rt];
-            mml[2 * rt + 1] = lsum[rt];
+            for (int dt = 0; dt < DT; ++dt) *(floatx4_v *)(mo + (rt * DT + dt) * 256) = acc_o[dt][rt];
+            mml[(2 * rt) * 64] = m_row[rt];
+            mml[(2 * rt + 1) * 64] = lsum[rt];
         }
     }
     __syncthreads();
     if (kp == 1) return;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        const float m1 = mml[2 * rt], l1 = mml[2 * rt + 1];
+        const float m1 = mml[(2 * rt) * 64], l1 = mml[(2 * rt + 1) * 64];
         const float M = fmaxf(m_row[rt], m1);
         const float f0 = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - M);
         const float f1 = (m1 == NEG_INF) ? 0.f : fast_exp2(m1 - M);
@@ -885,7 +889,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
         bf16_t *orow = out + ((int64_t)(q_begin + q0 + qi) * num_q_heads + g * G + hh) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const floatx4_v o1 = *(const floatx4_v *)(mo + (rt * DT + dt) * 4);
+            const floatx4_v o1 = *(const floatx4_v *)(mo + (rt * DT + dt) * 256);
             const floatx4_v o = (acc_o[dt][rt] * f0 + o1 * f1) * inv;
             uint2 v;
             v.x = pack_bf16x2(o[0], o[1]);
