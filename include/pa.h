@@ -38,6 +38,14 @@
  *     outside [0, num_blocks * block_size) is skipped, and context lengths are
  *     clamped to max_context_len (and to max_blocks_per_seq * block_size).
  *     Such inputs are caller errors and their results are unspecified.
+ *     With the environment variable PA_DEBUG set (to anything but "0"), every
+ *     entry point first copies the tables it will read to the host (after
+ *     the work already queued on its stream, so the call synchronises) and
+ *     checks them: table entries a context reaches inside [0, num_blocks),
+ *     0 <= context_lens <= max_context_len (prefill: queries per chunk <=
+ *     its context, cu_query_lens[0] == 0), slots inside the pool and distinct,
+ *     copy pairs inside their pools with distinct destinations.  A violation
+ *     returns PA_ERR_INVALID_ARG and launches nothing.
  *   - Supported: dtype PA_F32 or PA_BF16 (prefill: PA_BF16 only), head_dim
  *     64 or 128, block_size 16 or 32, num_q_heads / num_kv_heads in
  *     {1, 2, 4, 8}.  Other shapes return PA_ERR_UNSUPPORTED.

@@ -3,6 +3,11 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -207,6 +212,132 @@ bool device_view(const void *p, const void **dev) {
     return false;
 }
 
+// ---- PA_DEBUG=1: device-resident tables checked on the host ----------------
+// Copies the tables an entry point reads (after the work already queued on
+// the stream) and checks the preconditions the kernels assume; a violation
+// returns PA_ERR_INVALID_ARG before any launch.  Synchronises the stream.
+
+bool debug_checks() {
+    const char *e = getenv("PA_DEBUG");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+template <typename T>
+pa_status fetch(std::vector<T> &dst, const void *src, size_t n, hipStream_t stream,
+                const char *what) {
+    dst.resize(n);
+    if (n == 0) return PA_OK;
+    hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "PA_DEBUG: reading %s: %s", what, hipGetErrorString(e));
+    return PA_OK;
+}
+
+// Table rows: every entry a sequence of length L reads, [0, ceil(L / B)),
+// must name a block of the pool.
+pa_status check_table_rows(const std::vector<int32_t> &bt, const std::vector<int32_t> &lens,
+                           int32_t max_blocks, int32_t block_size, int64_t num_blocks,
+                           const char *what) {
+    for (size_t s = 0; s < lens.size(); ++s) {
+        const int64_t nb = (lens[s] + (int64_t)block_size - 1) / block_size;
+        for (int64_t j = 0; j < nb; ++j) {
+            const int32_t b = bt[s * (size_t)max_blocks + (size_t)j];
+            if (b < 0 || b >= num_blocks)
+                return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: %s[%zu][%lld] = %d outside [0, %lld)",
+                            what, s, (long long)j, b, (long long)num_blocks);
+        }
+    }
+    return PA_OK;
+}
+
+pa_status debug_decode(const pa::DecodeArgs &a, hipStream_t stream) {
+    if (a.num_seqs <= 0) return PA_OK;
+    std::vector<int32_t> lens, bt;
+    pa_status s = fetch(lens, a.context_lens, (size_t)a.num_seqs, stream, "context_lens");
+    if (s != PA_OK) return s;
+    for (int32_t i = 0; i < a.num_seqs; ++i)
+        if (lens[i] < 0 || lens[i] > a.max_context_len)
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: context_lens[%d] = %d outside [0, %d]", i,
+                        lens[i], a.max_context_len);
+    s = fetch(bt, a.block_tables, (size_t)a.num_seqs * a.max_blocks_per_seq, stream,
+              "block_tables");
+    if (s != PA_OK) return s;
+    return check_table_rows(bt, lens, a.max_blocks_per_seq, a.block_size, a.num_blocks,
+                            "block_tables");
+}
+
+pa_status debug_slots(const int64_t *slot_mapping, int32_t num_tokens, int64_t num_slots,
+                      hipStream_t stream) {
+    std::vector<int64_t> slots;
+    pa_status s = fetch(slots, slot_mapping, (size_t)num_tokens, stream, "slot_mapping");
+    if (s != PA_OK) return s;
+    std::vector<int64_t> used;
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        if (slots[t] < 0) continue;  // padding
+        if (slots[t] >= num_slots)
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: slot_mapping[%d] = %lld outside [0, %lld)",
+                        t, (long long)slots[t], (long long)num_slots);
+        used.push_back(slots[t]);
+    }
+    std::sort(used.begin(), used.end());
+    for (size_t i = 1; i < used.size(); ++i)
+        if (used[i] == used[i - 1])
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: slot %lld written twice",
+                        (long long)used[i]);
+    return PA_OK;
+}
+
+pa_status debug_prefill(const int32_t *cu_query_lens, const int32_t *context_lens,
+                        const int32_t *block_tables, int32_t num_chunks, int32_t max_query_len,
+                        int32_t max_blocks, int32_t block_size, int64_t num_blocks,
+                        hipStream_t stream) {
+    std::vector<int32_t> cu, lens, bt;
+    pa_status s = fetch(cu, cu_query_lens, (size_t)num_chunks + 1, stream, "cu_query_lens");
+    if (s == PA_OK) s = fetch(lens, context_lens, (size_t)num_chunks, stream, "context_lens");
+    if (s == PA_OK)
+        s = fetch(bt, block_tables, (size_t)num_chunks * max_blocks, stream, "block_tables");
+    if (s != PA_OK) return s;
+    if (cu[0] != 0) return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: cu_query_lens[0] = %d, not 0", cu[0]);
+    for (int32_t c = 0; c < num_chunks; ++c) {
+        const int32_t n = cu[c + 1] - cu[c];
+        if (n < 0 || n > max_query_len)
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: chunk %d has %d queries (max_query_len %d)",
+                        c, n, max_query_len);
+        if (n > lens[c] || (int64_t)lens[c] > (int64_t)max_blocks * block_size)
+            return fail(PA_ERR_INVALID_ARG,
+                        "PA_DEBUG: chunk %d: %d queries over context_lens %d (table holds %lld)",
+                        c, n, lens[c], (long long)max_blocks * block_size);
+    }
+    return check_table_rows(bt, lens, max_blocks, block_size, num_blocks, "block_tables");
+}
+
+pa_status debug_copy(const void *mapping, int32_t num_pairs, int64_t src_num_blocks,
+                     int64_t dst_num_blocks, bool same_pool, hipStream_t stream) {
+    std::vector<int64_t> m;
+    pa_status s = fetch(m, mapping, (size_t)num_pairs * 2, stream, "block_mapping");
+    if (s != PA_OK) return s;
+    std::vector<int64_t> dst, src;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        if (m[2 * i] < 0 || m[2 * i] >= src_num_blocks || m[2 * i + 1] < 0 ||
+            m[2 * i + 1] >= dst_num_blocks)
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: pair %d (%lld -> %lld) outside the pools", i,
+                        (long long)m[2 * i], (long long)m[2 * i + 1]);
+        src.push_back(m[2 * i]);
+        dst.push_back(m[2 * i + 1]);
+    }
+    std::sort(dst.begin(), dst.end());
+    for (size_t i = 1; i < dst.size(); ++i)
+        if (dst[i] == dst[i - 1])
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: destination block %lld written twice",
+                        (long long)dst[i]);
+    if (same_pool)
+        for (int64_t b : src)
+            if (std::binary_search(dst.begin(), dst.end(), b))
+                return fail(PA_ERR_INVALID_ARG,
+                            "PA_DEBUG: block %lld is both a source and a destination", (long long)b);
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +376,11 @@ pa_status pa_reshape_and_cache(const void *key, const void *value, void *key_cac
     CHECK_PTR(key_cache, 16);
     CHECK_PTR(value_cache, 16);
     CHECK_PTR(slot_mapping, 8);
+    if (debug_checks()) {
+        const pa_status d = debug_slots(slot_mapping, num_tokens, num_blocks * block_size,
+                                        (hipStream_t)stream);
+        if (d != PA_OK) return d;
+    }
     return hip_status(pa::launch_reshape_and_cache(key, value, key_cache, value_cache,
                                                    slot_mapping, num_tokens, num_kv_heads,
                                                    head_dim, block_size, num_blocks,
@@ -290,6 +426,7 @@ pa_status pa_decode_partitions(void *out, const void *query, const void *key_cac
                                block_size, max_blocks_per_seq, num_blocks, max_context_len,
                                partition_size, scale, dtype, workspace, workspace_bytes, true);
     if (s != PA_OK) return s;
+    if (debug_checks() && (s = debug_decode(st.a, (hipStream_t)stream)) != PA_OK) return s;
     return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
                       "decode_partitions");
 }
@@ -321,6 +458,7 @@ pa_status pa_decode(void *out, const void *query, const void *key_cache,
                                block_size, max_blocks_per_seq, num_blocks, max_context_len,
                                partition_size, scale, dtype, workspace, workspace_bytes, true);
     if (s != PA_OK) return s;
+    if (debug_checks() && (s = debug_decode(st.a, (hipStream_t)stream)) != PA_OK) return s;
     s = hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream), "decode_partitions");
     if (s != PA_OK) return s;
     return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
@@ -347,6 +485,7 @@ pa_status pa_decode_append_partitions(void *out, const void *query, const void *
     }
     st.a.new_key = new_key;
     st.a.new_value = new_value;
+    if (debug_checks() && (s = debug_decode(st.a, (hipStream_t)stream)) != PA_OK) return s;
     return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
                       "decode_append_partitions");
 }
@@ -391,6 +530,11 @@ pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, void *key
     CHECK_PTR(key_cache, 16);
     CHECK_PTR(value_cache, 16);
     CHECK_PTR(slot_mapping, 8);
+    if (debug_checks()) {
+        const pa_status d = debug_slots(slot_mapping, num_tokens, num_blocks * block_size,
+                                        (hipStream_t)stream);
+        if (d != PA_OK) return d;
+    }
     return hip_status(pa::launch_reshape_and_cache_fp8(
                           key, value, key_cache, value_cache, slot_mapping, num_tokens,
                           num_kv_heads, head_dim, block_size, num_blocks,
@@ -421,6 +565,7 @@ pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key
     st.a.kv_fp8 = 1;
     st.a.k_scale = k_scale;
     st.a.v_scale = v_scale;
+    if (debug_checks() && (s = debug_decode(st.a, (hipStream_t)stream)) != PA_OK) return s;
     return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
                       "decode_fp8_partitions");
 }
@@ -451,6 +596,7 @@ pa_status pa_decode_fp8_append_partitions(
     st.a.v_scale = v_scale;
     st.a.new_key = new_key;
     st.a.new_value = new_value;
+    if (debug_checks() && (s = debug_decode(st.a, (hipStream_t)stream)) != PA_OK) return s;
     return hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
                       "decode_fp8_append_partitions");
 }
@@ -518,6 +664,12 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
     CHECK_PTR(context_lens, 4);
     if (!pa::prefill_shape_supported(head_dim, block_size, num_q_heads / num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "prefill shape not supported");
+    if (debug_checks()) {
+        const pa_status d = debug_prefill(cu_query_lens, context_lens, block_tables, num_chunks,
+                                          max_query_len, max_blocks_per_seq, block_size,
+                                          num_blocks, (hipStream_t)stream);
+        if (d != PA_OK) return d;
+    }
     pa::PrefillArgs a;
     a.out = out;
     a.query = query;
@@ -568,6 +720,12 @@ pa_status pa_prefill_chunk_fp8(void *out, const void *query, const void *key_cac
     CHECK_PTR(context_lens, 4);
     if (!pa::prefill_shape_supported(head_dim, block_size, num_q_heads / num_kv_heads))
         return fail(PA_ERR_UNSUPPORTED, "prefill shape not supported");
+    if (debug_checks()) {
+        const pa_status d = debug_prefill(cu_query_lens, context_lens, block_tables, num_chunks,
+                                          max_query_len, max_blocks_per_seq, block_size,
+                                          num_blocks, (hipStream_t)stream);
+        if (d != PA_OK) return d;
+    }
     pa::PrefillArgs a;
     a.out = out;
     a.query = query;
@@ -617,6 +775,11 @@ pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,
             return fail(PA_ERR_INVALID_ARG,
                         "%s is neither device memory nor pinned host memory the device can map",
                         names[i]);
+    if (debug_checks()) {
+        const pa_status d = debug_copy(dev[4], num_pairs, src_num_blocks, dst_num_blocks,
+                                       src_key_cache == dst_key_cache, (hipStream_t)stream);
+        if (d != PA_OK) return d;
+    }
     return hip_status(pa::launch_copy_blocks(dev[0], dev[1], (void *)dev[2], (void *)dev[3],
                                              (const int64_t *)dev[4], num_pairs, src_num_blocks,
                                              dst_num_blocks, block_bytes, (hipStream_t)stream),
