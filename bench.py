@@ -369,7 +369,9 @@ def main():
                                       "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                                       "traffic": measured_traffic(
                                           pf_kernel, case.name + ("_fp8" if fp8 else "")),
-                                      "algorithmic_flops_per_launch": pf_flops}
+                                      "algorithmic_flops_per_launch": pf_flops,
+                                      "query_tokens_per_s": round(
+                                          sum(n for n, _ in chunks) / (t_pf * 1e-3), 1)}
     if T and not fused:
         result["cache_write"] = {"ms": round(t_cw, 5), "bytes": cw_bytes,
                                  "GB/s": round(cw_bytes / (t_cw * 1e-3) / 1e9, 1)}
