@@ -194,12 +194,15 @@ def test_one_hot_every_token_tiny():
         assert torch.equal(out.cpu(), want), (t, out[:, :, :4].cpu(), want[:, :, :4])
 
 
-@pytest.mark.parametrize("name", ["llama8b_decode", "long_context_decode"])
+@pytest.mark.parametrize("name", ["llama8b_decode", "long_context_decode", "mixed_chunked_prefill",
+                                  "prefix_sharing_decode"])
 def test_one_hot_sampled_large(name):
     c = W.NAMED[name]()
     gen = torch.Generator().manual_seed(9)
+    # Shared prefix blocks hold one code for all sequences: aim at own tokens.
+    lo = c.shared_blocks.numel() * c.block_size if c.shared_blocks is not None else 0
     for rep in range(3):
-        targets = [int(torch.randint(0, int(L), (1,), generator=gen)) for L in c.context_lens]
+        targets = [int(torch.randint(lo, int(L), (1,), generator=gen)) for L in c.context_lens]
         if rep == 0:
             targets = [int(L) - 1 for L in c.context_lens]
         q, kc, vc, want = _one_hot_probe(c, targets, "bf16")
