@@ -140,3 +140,9 @@ def test_append_rejects_bad_rows():
     with pytest.raises(ValueError):
         binding.decode_append(torch.empty_like(q), q, bad, bad, kc, vc, dev(c.block_tables),
                               dev(c.context_lens), c.scale, 50)
+
+
+def test_append_at_max_balanced_batch():
+    """8192 sequences, the largest batch the balanced split takes: every new
+    row lands in its slot and is attended to."""
+    check_case(W.random_case(117, "bf16", 8192, 8, 2, 128, 16, 1, 40), "8192 seqs")

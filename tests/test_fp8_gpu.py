@@ -397,6 +397,18 @@ def test_fp8_append_parity_shapes(D, B, G):
     assert (out[0] == 0).all()                      # empty context: zeros, nothing written
 
 
+def test_fp8_decode_at_max_balanced_batch():
+    """8192 sequences, the largest batch the FP8 decode takes."""
+    c = W.random_case(312, "bf16", 8192, 8, 2, 128, 16, 1, 40, write_new=False)
+    ks, vs = 0.05, 0.05
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    poison_tails(c, kc8, vc8)
+    ref = oracle.decode_fp8(c.query, kc8, vc8, c.block_tables, c.context_lens, c.scale, ks, vs)
+    say("fp8 decode 8192 seqs")
+    out = gpu_decode_fp8(c, kc8, vc8, ks, vs)
+    check_close(out, ref, "bf16", "fp8 8192 seqs")
+
+
 def test_fp8_append_many_short_sequences():
     """Hundreds of 1..40-token sequences: several new rows per 64-unit chunk."""
     c = W.random_case(311, "bf16", 300, 8, 2, 128, 16, 1, 40, extra_blocks=5)

@@ -133,6 +133,17 @@ def test_decode_large_batch_uses_fixed_partitions():
     check_close(out, oracle_decode(c, c.key_cache, c.value_cache), "bf16", "8200 seqs")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_decode_balanced_split_at_max_batch(dtype, D):
+    """8192 sequences, the largest batch the balanced split takes: its unit
+    scan fills the LDS array, and most waves cross many pair boundaries."""
+    c = W.random_case(116, dtype, 8192, 8, 2, D, 16, 1, 40, write_new=False)
+    say("max balanced batch", dtype, c.num_seqs)
+    out = gpu_decode(c, dev(c.key_cache), dev(c.value_cache))
+    torch.cuda.synchronize()
+    check_close(out, oracle_decode(c, c.key_cache, c.value_cache), dtype, "8192 seqs")
+
+
 def test_decode_deterministic():
     c = W.llama8b_decode(num_seqs=16)
     kc, vc = dev(c.key_cache), dev(c.value_cache)
