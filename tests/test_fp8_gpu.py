@@ -257,6 +257,23 @@ def test_fp8_prefill_parity_shapes(D, B, G):
     check_close(out, ref, "bf16", f"fp8 prefill D{D} B{B} G{G}")
 
 
+def test_fp8_prefill_empty_long_and_many_chunks():
+    """An empty chunk, a 2,048-query chunk over 6,000 keys, a one-key context
+    and 40 small ragged chunks in one launch, NaN codes past every context."""
+    chunks = [(3, 10), (0, 50), (2048, 6000), (1, 1)] + \
+        [(k % 37 + 1, 100 + 13 * k) for k in range(40)]
+    c = W.make_case("pf8 edge", 78, "bf16", 8, 2, 128, 16, [5], new_positions=[4],
+                    chunks=chunks, extra_blocks=3)
+    ks, vs = 1.0 / 64, 1.0 / 32
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    poison_chunk_tails(c, kc8, vc8)
+    say("fp8 prefill empty, long and many chunks")
+    out = gpu_prefill_fp8(c, kc8, vc8, ks, vs)
+    ref = oracle.prefill_fp8(c.chunk_query, kc8, vc8, c.chunk_block_tables, c.chunk_cu_query_lens,
+                             c.chunk_context_lens, c.scale, ks, vs)
+    check_close(out, ref, "bf16", "fp8 prefill edge chunks")
+
+
 def test_fp8_prefill_mixed_workload():
     """The mixed chunked-prefill shape (2 chunks of 512 queries over 2,048 prior
     tokens, 32 q / 8 kv heads, d 128, B 16): the chunks' own tokens are written

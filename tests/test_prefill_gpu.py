@@ -44,6 +44,23 @@ def test_prefill_parity_shapes(D, B, G):
     check_close(out, ref, "bf16", f"prefill D{D} B{B} G{G}")
 
 
+# An empty chunk, a 2,048-query chunk over 6,000 keys (64 tiles of queries),
+# a one-key context and 40 small ragged chunks, all in one launch.
+EDGE_CHUNKS = [(3, 10), (0, 50), (2048, 6000), (1, 1)] + \
+    [(k % 37 + 1, 100 + 13 * k) for k in range(40)]
+
+
+def test_prefill_empty_long_and_many_chunks():
+    c = W.make_case("pf edge", 77, "bf16", 8, 2, 128, 16, [5], new_positions=[4],
+                    chunks=EDGE_CHUNKS, extra_blocks=3)
+    kc, vc = dev(c.key_cache), dev(c.value_cache)
+    apply_cache_write_gpu(c, kc, vc)
+    say("prefill empty, long and many chunks")
+    out = gpu_prefill(c, kc, vc)
+    torch.cuda.synchronize()
+    check_close(out, oracle_prefill(c, *oracle_pools(c)), "bf16", "prefill edge chunks")
+
+
 def test_prefill_mixed_workload():
     c = W.mixed_chunked_prefill()
     kc, vc = dev(c.key_cache), dev(c.value_cache)
