@@ -366,6 +366,31 @@ def test_fp8_decode_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_fp8_decode_phases_equal_decode():
+    """pa_decode_fp8_partitions then pa_decode_reduce gives pa_decode_fp8's
+    output bit for bit, on ragged lengths from empty to many pairs per wave."""
+    lens = [0, 1, 15, 16, 17, 300, 4097, 33] + [int(x) for x in torch.randint(
+        1, 3000, (40,), generator=torch.Generator().manual_seed(12))]
+    c = W.make_case("fp8 phases", 313, "bf16", 32, 8, 128, 16, lens, extra_blocks=2)
+    ks, vs = 0.05, 0.05
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    poison_tails(c, kc8, vc8)
+    say("fp8 decode phases")
+    a = gpu_decode_fp8(c, kc8, vc8, ks, vs)
+    q, gk, gv = dev(c.query), dev(kc8), dev(vc8)
+    b = torch.full_like(q, float("nan"))
+    maxL = int(c.context_lens.max())
+    bt, ln = dev(c.block_tables), dev(c.context_lens)
+    ws = binding.make_fp8_workspace(q, gk, maxL)
+    binding.decode_fp8_partitions(b, q, gk, gv, bt, ln, c.scale, maxL, ks, vs, ws)
+    binding.decode_reduce(b, ln, c.num_kv_heads, c.block_size, c.block_tables.shape[1], maxL, 0,
+                          ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.decode_fp8(c.query, kc8, vc8, c.block_tables, c.context_lens, c.scale, ks, vs)
+    check_close(a, ref, "bf16", "fp8 phases vs oracle")
+
+
 # ------------------------------------------------ decode with append (fused) --
 
 def _fp8_append_vs_oracle(c, ks, vs, kc8, vc8, split=False):
