@@ -329,6 +329,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
         for (int hp = 0; hp < 2 / NH; ++hp) {
             const int kt0 = hp * NKT;  // first 16-key tile of the pass
             floatx4_v s[NKT][RT];
+            __builtin_amdgcn_s_setprio(0);  // products at the base priority
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
                 u32x4 kf[KS];
@@ -344,6 +345,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
                     s[kt][rt] = a;
                 }
             }
+            // The softmax runs at a raised priority: the SIMD's other wave
+            // keeps the matrix core busy meanwhile, and this wave's vector
+            // work is not held back behind it.
+            __builtin_amdgcn_s_setprio(1);
             // Causal mask: only passes that reach past the tile's first
             // position need it (a uniform branch).  Masked logits are -inf,
             // never scaled.
@@ -418,6 +423,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
                 }
             };
             issue_v(vb[0], 0);
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int b = 0; b < DT / VB; ++b) {
                 lds_wait(vb[b & 1]);
@@ -435,6 +441,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
                                 mfma16x16x32(vf, pf[rt][h], acc_o[VB * b + j][rt]);
                     }
             }
+            __builtin_amdgcn_s_setprio(1);
         }
     };
 
@@ -738,6 +745,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
     auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
                        uint64_t seg_phys) __attribute__((always_inline)) {
         floatx4_v s[4][RT];
+        __builtin_amdgcn_s_setprio(0);  // products at the base priority, softmax raised
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
             const int key = (kt >> 1) * 32 + 8 * (l16 >> 2) + (l16 & 3) + 4 * (kt & 1);
@@ -757,6 +765,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
                 s[kt][rt] = a;
             }
         }
+        __builtin_amdgcn_s_setprio(1);
         // Causal mask (key of element i of tile kt: see the key order above).
         if (key0 + kKeyBlock - 1 > pos0) {
 #pragma unroll
@@ -803,6 +812,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
             for (int h = 0; h < 2; ++h) acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
         }
         if (dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
+        __builtin_amdgcn_s_setprio(0);
         // O^T += V^T P^T: dim dt * 16 + l16, keys 32 h + 8 lg + [0, 8).
         const bool tail = key0 + kKeyBlock > kend;
         uint32_t vmask[2][2];  // [half][word]: bytes of keys past kend are cleared
@@ -826,6 +836,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
                     acc_o[dt][rt] = mfma16x16x32(vf, pf[rt][h], acc_o[dt][rt]);
             }
         }
+        __builtin_amdgcn_s_setprio(1);
     };
 
     auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
