@@ -69,7 +69,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, inconsistent shape */
     PA_ERR_UNSUPPORTED = 2,  /* dtype, head_dim, block_size or group size not built */
     PA_ERR_WORKSPACE = 3,    /* decode workspace missing or too small */
-    PA_ERR_HIP = 4           /* the HIP runtime refused the launch */
+    PA_ERR_HIP = 4,          /* the HIP runtime refused the launch */
+    PA_ERR_POOL_EXHAUSTED = 5  /* block manager: too few free blocks (nothing changed) */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -241,7 +242,9 @@ pa_status pa_decode_append_partitions(void *out, const void *query, const void *
  * position context_lens[c] - n_c + i and attends to keys 0 .. that position.
  * block_tables has one row per chunk.  max_query_len >= every n_c sizes the
  * launch.  bf16 only: QK^T and PV run on the matrix cores (bf16 inputs, fp32
- * accumulation), softmax in fp32, out in bf16.
+ * accumulation), softmax in fp32, out in bf16.  scale must be positive and
+ * finite (the attention scale 1 / sqrt(head_dim) of the pages is); other
+ * values return PA_ERR_INVALID_ARG.
  */
 pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
                            const void *value_cache, const int32_t *block_tables,
@@ -381,7 +384,7 @@ pa_status pa_decode_fp8_append_partitions(
  * products run on the bf16 matrix cores (the codes widen to bf16 exactly).
  * The chunk's own new keys and values must already be in the pools
  * (pa_reshape_and_cache_fp8).  Other arguments, conventions and errors as
- * pa_prefill_chunk; scales must be positive and finite.
+ * pa_prefill_chunk; scale, k_scale and v_scale must be positive and finite.
  */
 pa_status pa_prefill_chunk_fp8(void *out, const void *query, const void *key_cache,
                                const void *value_cache, const int32_t *block_tables,
@@ -425,8 +428,8 @@ pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key
  * freed block that is in the prefix index stays reusable until the pool hands
  * it out again.  All calls are host-only, synchronous and not thread-safe
  * (one manager per scheduler thread).  Errors: PA_ERR_INVALID_ARG (bad
- * argument or unknown / duplicate sequence id), PA_ERR_WORKSPACE (the pool
- * has too few free blocks; nothing was changed).
+ * argument or unknown / duplicate sequence id), PA_ERR_POOL_EXHAUSTED (the
+ * pool has too few free blocks; nothing was changed).
  */
 typedef struct pa_block_manager pa_block_manager;
 
@@ -453,7 +456,12 @@ void pa_bm_destroy(pa_block_manager *bm);
  * entries) receives the slot (block * block_size + offset) of prompt token t
  * for pa_reshape_and_cache, or -1 when the token's block came from the prefix
  * cache (its keys and values are already in the pool).  *num_cached_tokens
- * (optional) receives that count.
+ * (optional) receives that count.  At most (num_tokens - 1) / block_size
+ * leading blocks are reused, so the prompt's last token always gets a slot
+ * and a query row to compute (its output gives the next token).  Reused
+ * blocks that are cached but free count against the free pool: when the
+ * pool cannot hold the rest, PA_ERR_POOL_EXHAUSTED is returned before any
+ * change.
  */
 pa_status pa_bm_add_sequence(pa_block_manager *bm, int64_t seq_id, const int32_t *tokens,
                              int32_t num_tokens, int64_t *slot_mapping,
@@ -492,7 +500,7 @@ pa_status pa_bm_block_table(const pa_block_manager *bm, int64_t seq_id, int32_t 
  * One decode step for a batch: appends tokens[i] to seq_ids[i] (distinct
  * ids) in order, as pa_bm_append, and writes the slots (the step's
  * slot_mapping).  The blocks the step needs are checked first: on
- * PA_ERR_WORKSPACE or PA_ERR_INVALID_ARG nothing has changed.
+ * PA_ERR_POOL_EXHAUSTED or PA_ERR_INVALID_ARG nothing has changed.
  */
 pa_status pa_bm_append_batch(pa_block_manager *bm, const int64_t *seq_ids,
                              const int32_t *tokens, int32_t n, int64_t *slots);

@@ -109,14 +109,17 @@ class ReferenceBlockManager:
         nblk = -(-n // B)
         table = []
         if self.prefix_cache:
-            for j in range(n // B):
+            # the last prompt token always gets a slot (its query row gives
+            # the next token), so at most (n - 1) // B blocks are reused
+            for j in range(max(0, n - 1) // B):
                 key = self._key(table[-1] if table else -1, tokens[j * B:(j + 1) * B])
                 b = self.index.get(key)
                 if b is None:
                     break
                 table.append(b)
         reused = len(table)
-        if self.free_count < nblk - reused:
+        reclaim = sum(1 for b in table if self.ref[b] == 0)  # cached but free
+        if self.free_count - reclaim < nblk - reused:
             raise PoolExhausted
         for b in table:
             if self.ref[b] == 0:

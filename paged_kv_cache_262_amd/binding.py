@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpa.so"
 _lib = None
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+(PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
+ PA_ERR_POOL_EXHAUSTED) = range(6)
 PA_F32, PA_BF16 = 0, 1
 _DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 

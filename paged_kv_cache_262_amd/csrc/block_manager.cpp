@@ -36,6 +36,7 @@
 #include <deque>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "pa.h"
@@ -186,8 +187,12 @@ pa_status pa_bm_add_sequence(pa_block_manager *bm, int64_t seq_id, const int32_t
     Sequence s;
     int64_t reused = 0;
     uint64_t h = 0;
+    // At most (num_tokens - 1) / B leading blocks are reused, so the prompt's
+    // last token always has a slot: its query row must be computed to give
+    // the logits of the next token.
+    const int64_t max_reuse = num_tokens > 0 ? (num_tokens - 1) / B : 0;
     if (bm->prefix_cache) {
-        for (int64_t j = 0; j + 1 <= num_tokens / B; ++j) {
+        for (int64_t j = 0; j < max_reuse; ++j) {
             const uint64_t hj = hash_block(h, tokens + j * B, B);
             const int32_t b = bm->lookup(hj, tokens + j * B, j > 0 ? s.table[j - 1] : -1);
             if (b < 0) break;
@@ -196,7 +201,11 @@ pa_status pa_bm_add_sequence(pa_block_manager *bm, int64_t seq_id, const int32_t
             ++reused;
         }
     }
-    if (bm->free_count < nblk - reused) return PA_ERR_WORKSPACE;  // pool exhausted
+    // Reused blocks that are cached but free (count 0) leave the free pool
+    // too: they are counted before any state changes.
+    int64_t reclaim = 0;
+    for (int64_t j = 0; j < reused; ++j) reclaim += bm->blocks[s.table[j]].ref == 0;
+    if (bm->free_count - reclaim < nblk - reused) return PA_ERR_POOL_EXHAUSTED;
     for (int64_t j = 0; j < reused; ++j) {
         const int32_t b = s.table[j];
         if (bm->blocks[b].ref == 0) {  // cached but free: take it back from the pool
@@ -227,12 +236,12 @@ pa_status pa_bm_append(pa_block_manager *bm, int64_t seq_id, int32_t token, int6
     const int B = bm->block_size;
     const int64_t off = s.len % B;
     if (off == 0) {  // a new block
-        if (bm->free_count < 1) return PA_ERR_WORKSPACE;
+        if (bm->free_count < 1) return PA_ERR_POOL_EXHAUSTED;
         s.table.push_back(bm->take_free());
     } else {
         const int32_t last = s.table.back();
         if (bm->blocks[last].ref > 1) {  // shared and partly filled: copy on write
-            if (bm->free_count < 1) return PA_ERR_WORKSPACE;
+            if (bm->free_count < 1) return PA_ERR_POOL_EXHAUSTED;
             const int32_t fresh = bm->take_free();
             bm->copies.push_back(last);
             bm->copies.push_back(fresh);
@@ -298,15 +307,16 @@ pa_status pa_bm_append_batch(pa_block_manager *bm, const int64_t *seq_ids,
     // where it is shared and partly filled.  Checked up front, so a failed
     // call changes nothing.
     int64_t need = 0;
+    std::unordered_set<int64_t> ids;  // one token per sequence: duplicates rejected
+    ids.reserve((size_t)n);
     for (int32_t i = 0; i < n; ++i) {
         auto it = bm->seqs.find(seq_ids[i]);
         if (it == bm->seqs.end()) return PA_ERR_INVALID_ARG;
-        for (int32_t k = 0; k < i; ++k)
-            if (seq_ids[k] == seq_ids[i]) return PA_ERR_INVALID_ARG;  // one token per sequence
+        if (!ids.insert(seq_ids[i]).second) return PA_ERR_INVALID_ARG;
         const Sequence &sq = it->second;
         if (sq.len % bm->block_size == 0 || bm->blocks[sq.table.back()].ref > 1) ++need;
     }
-    if (bm->free_count < need) return PA_ERR_WORKSPACE;
+    if (bm->free_count < need) return PA_ERR_POOL_EXHAUSTED;
     for (int32_t i = 0; i < n; ++i) {
         const pa_status st = pa_bm_append(bm, seq_ids[i], tokens[i], slots + i);
         if (st != PA_OK) return st;  // not reached: checked above

@@ -351,6 +351,7 @@ const char *pa_status_string(int32_t status) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
         case PA_ERR_HIP: return "PA_ERR_HIP";
+        case PA_ERR_POOL_EXHAUSTED: return "PA_ERR_POOL_EXHAUSTED";
     }
     return "PA_UNKNOWN_STATUS";
 }
@@ -654,7 +655,8 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
     if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
     if (num_chunks == 0 || max_query_len == 0) return PA_OK;
     if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(scale > 0.0f) || !isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "prefill scale must be positive and finite");
     CHECK_PTR(out, 16);
     CHECK_PTR(query, 16);
     CHECK_PTR(key_cache, 16);
@@ -710,7 +712,8 @@ pa_status pa_prefill_chunk_fp8(void *out, const void *query, const void *key_cac
     if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
     if (num_chunks == 0 || max_query_len == 0) return PA_OK;
     if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks <= 0");
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(scale > 0.0f) || !isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "prefill scale must be positive and finite");
     CHECK_PTR(out, 16);
     CHECK_PTR(query, 16);
     CHECK_PTR(key_cache, 16);

@@ -511,6 +511,44 @@ def pin_fp8_encode_rounding(lib):
         assert abs(abs(di) - a) <= np.min(np.abs(finite - a)) + 0.0
 
 
+def _nearest_e4m3(y):
+    """Code of the e4m3 value nearest to y (ties to the even code, saturating at
+    448), by a search over the format table; written apart from the oracle."""
+    vals = _e4m3_table()
+    sign = 0x80 if math.copysign(1.0, y) < 0 else 0
+    a = min(abs(y), 448.0)
+    best, best_d = None, None
+    for c in range(0x7F):
+        d = abs(vals[c] - a)
+        if best_d is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    return sign | best
+
+
+def pin_fp8_scale_is_one_reciprocal_multiply(lib):
+    """The stored code is that of x * fp32(1 / scale), one fp32 multiply by the
+    reciprocal (the FP8 reading of the build).  At these two (x, scale) pairs
+    the fp32 product and the fp32 quotient x / scale fall on opposite sides
+    of the midpoint 7.5 * 2^-9 between codes 0x07 and 0x08, so the two
+    readings give different codes; expected codes come from numpy fp32
+    arithmetic and the format table."""
+    cases = [(0.00439453125, 0.3), (0.02490234375, 1.7)]
+    for x, s in cases:
+        xf, sf = np.float32(x), np.float32(s)
+        want = _nearest_e4m3(float(xf * (np.float32(1.0) / sf)))
+        other = _nearest_e4m3(float(xf / sf))
+        assert want != other, (x, s)          # the case separates the readings
+        assert oracle.fp8_encode(torch.tensor([x, -x]), s, lib=lib).tolist() == [want, 0x80 | want]
+        # the cache write (K row and transposed V page) takes the same reading
+        key = torch.full((1, 1, 64), x)
+        kc0 = torch.zeros((2, 1, 16, 64), dtype=torch.uint8)
+        vc0 = torch.zeros((2, 1, 64, 16), dtype=torch.uint8)
+        kc, vc = oracle.reshape_and_cache_fp8(key, -key, kc0, vc0, [16 + 3], s, s, lib=lib)
+        assert torch.all(kc[1, 0, 3, :] == want) and torch.all(vc[1, 0, :, 3] == (0x80 | want))
+    assert [_nearest_e4m3(float(np.float32(x) * (np.float32(1.0) / np.float32(s))))
+            for x, s in cases] == [0x08, 0x07]
+
+
 def pin_fp8_cache_write_layout(lib):
     """K lands at [block][head][offset][d], V transposed at [block][head][d][offset],
     each the code of value / scale; untouched bytes keep their value."""
@@ -610,6 +648,7 @@ ALL_PINS = [
     pin_copy_blocks_rejects,
     pin_fp8_code_values,
     pin_fp8_encode_rounding,
+    pin_fp8_scale_is_one_reciprocal_multiply,
     pin_fp8_cache_write_layout,
     pin_fp8_decode_equals_dequantized_decode,
     pin_fp8_prefill_equals_dequantized_prefill,

@@ -42,9 +42,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.pa_abi_version() == 1
-    names = [lib.pa_status_string(i).decode() for i in range(5)]
+    names = [lib.pa_status_string(i).decode() for i in range(6)]
     assert names == ["PA_OK", "PA_ERR_INVALID_ARG", "PA_ERR_UNSUPPORTED", "PA_ERR_WORKSPACE",
-                     "PA_ERR_HIP"]
+                     "PA_ERR_HIP", "PA_ERR_POOL_EXHAUSTED"]
 
 
 def test_auto_partition_and_workspace(lib):
@@ -113,6 +113,10 @@ def test_prefill_rejects(lib):
     assert f(*bad, 1, None) == INVALID
     bad = list(args); bad[8] = -1                      # max_query_len
     assert f(*bad, 1, None) == INVALID
+    for sc in (0.0, -0.1, float("inf"), float("nan")):  # the scale must be positive, finite
+        bad = list(args); bad[15] = sc
+        assert f(*bad, 1, None) == INVALID, sc
+        assert "scale" in lib.pa_last_error().decode()
 
 
 def test_binding_refuses_cpu_tensors(lib):
@@ -170,6 +174,9 @@ def test_fp8_prefill_rejects(lib):
     args = [A, A, A, A, A, A, A, 2, 512, 32, 8, 128, 16, 160, 1000, 0.1]
     assert f(*args, 0.0, 1.0, None) == INVALID                     # scale must be positive
     assert f(*args, 1.0, float("nan"), None) == INVALID
+    for sc in (0.0, -0.1):                                          # so must the attention scale
+        bad = list(args); bad[15] = sc
+        assert f(*bad, 1.0, 1.0, None) == INVALID, sc
     bad = list(args); bad[9] = 7                                    # 32 % 7
     assert f(*bad, 1.0, 1.0, None) == INVALID
     bad = list(args); bad[11] = 96

@@ -204,3 +204,81 @@ def test_batch_calls_equal_single_calls():
     assert small.stats()["seq_tokens"] == 8 and small.stats()["free_blocks"] == 1
     a.close()
     small.close()
+
+
+def test_reused_free_blocks_count_against_the_pool():
+    """A prompt that reuses a cached block whose count is 0 takes that block
+    out of the free pool too: a 2-block pool with block 0 cached and free
+    cannot hold a 33-token prompt (3 blocks, 1 reused), and the call changes
+    nothing (model and library, with the pool-exhausted status)."""
+    B = 16
+    a = list(range(100, 116))                       # one full block
+    b = a + list(range(200, 217))                   # 33 tokens: reuses a's block
+    ref = ReferenceBlockManager(2, B, True)
+    lib = binding.BlockManager(2, B, prefix_cache=True)
+    for m in (ref, lib):
+        m.add_sequence(0, a)
+        m.free(0)
+    before = ref.stats()
+    assert lib.stats() == before and before["free_blocks"] == 2 and before["cached_blocks"] == 1
+    with pytest.raises(PoolExhausted):
+        ref.add_sequence(1, b)
+    with pytest.raises(binding.PAError) as e:
+        lib.add_sequence(1, b)
+    assert e.value.status == binding.PA_ERR_POOL_EXHAUSTED
+    assert ref.stats() == before and lib.stats() == before
+    # with one more block the same prompt fits: block 0 reused, two fresh ones
+    ref3 = ReferenceBlockManager(3, B, True)
+    lib3 = binding.BlockManager(3, B, prefix_cache=True)
+    for m in (ref3, lib3):
+        m.add_sequence(0, a)
+        m.free(0)
+    r = ref3.add_sequence(1, b)
+    assert lib3.add_sequence(1, b) == r
+    assert r[1] == 16 and -1 not in r[0][16:]
+    assert lib3.block_table(1) == (ref3.tables[1], 33) and ref3.tables[1][0] == 0
+    lib.close()
+    lib3.close()
+
+
+def test_last_prompt_token_is_never_cached():
+    """A prompt made only of cached full blocks still gets its last block
+    computed: reuse stops at (n - 1) // B blocks, so the last prompt token has
+    a slot and a query row (its output gives the next token)."""
+    B = 16
+    p = list(range(32))
+    ref = ReferenceBlockManager(8, B, True)
+    lib = binding.BlockManager(8, B, prefix_cache=True)
+    for m in (ref, lib):
+        m.add_sequence(0, p)
+    r = ref.add_sequence(1, p)
+    assert lib.add_sequence(1, p) == r
+    slots, cached = r
+    assert cached == 16 and slots[:16] == [-1] * 16
+    assert all(s >= 0 for s in slots[16:])
+    assert ref.tables[1][0] == ref.tables[0][0] and ref.tables[1][1] != ref.tables[0][1]
+    # one token more than the cached blocks: both blocks reused
+    r2 = ref.add_sequence(2, p + [7])
+    assert lib.add_sequence(2, p + [7]) == r2 and r2[1] == 32 and r2[0][32] >= 0
+    # a one-block prompt never reuses
+    r3 = ref.add_sequence(3, p[:16])
+    assert lib.add_sequence(3, p[:16]) == r3 and r3[1] == 0
+    assert lib.stats() == ref.stats()
+    lib.close()
+
+
+def test_append_batch_rejects_duplicates_in_large_batches():
+    """The duplicate-id check of a batch step scales to the largest decode
+    batches (8,192 sequences), and a duplicate anywhere is rejected."""
+    lib = binding.BlockManager(20000, 16)
+    n = 8192
+    for s in range(n):
+        lib.add_sequence(s, [1, 2, 3])
+    ids = list(range(n))
+    slots = lib.append_batch(ids, [5] * n)
+    assert slots.numel() == n
+    with pytest.raises(binding.PAError) as e:
+        lib.append_batch(ids[:-1] + [17], [5] * n)
+    assert e.value.status == binding.PA_ERR_INVALID_ARG
+    assert lib.stats()["seq_tokens"] == 4 * n
+    lib.close()

@@ -599,3 +599,40 @@ def test_fp8_block_manager_drives_decode():
         ref = oracle.decode_fp8(q, rk8, rv8, rbt, lens, DD ** -0.5, ks, vs)
         check_close(out, ref, "bf16", f"fp8 block manager step {step}")
     bm.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fp8_scale_reading_separating_values(dtype):
+    """Values whose code differs between x * fp32(1 / scale) (the library's
+    reading) and x / scale: 0.00439453125 at scale 0.3 -> 0x08 and
+    0.02490234375 at scale 1.7 -> 0x07 (the quotient gives 0x07 and 0x08).
+    Written through pa_reshape_and_cache_fp8 and through the fused FP8 decode
+    step, bit-exact against the oracle and against those codes."""
+    T, Hkv, D, B = 4, 2, 64, 16
+    x = torch.tensor([0.00439453125, 0.02490234375])
+    for (ks, vs), (xk, xv), (ck, cv) in (((0.3, 1.7), (x[0], x[1]), (0x08, 0x07)),
+                                         ((1.7, 0.3), (x[1], x[0]), (0x07, 0x08))):
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        key = torch.full((T, Hkv, D), float(xk)).to(tdt)
+        val = torch.full((T, Hkv, D), float(xv)).to(tdt)
+        key[1::2] = -key[1::2]
+        kc8 = torch.full((2, Hkv, B, D), 0x55, dtype=torch.uint8)
+        vc8 = torch.full((2, Hkv, D, B), 0x55, dtype=torch.uint8)
+        slots = torch.tensor([0, 5, 16, 31], dtype=torch.int64)
+        say("fp8 scale reading, cache write", dtype, ks, vs)
+        gk, gv = dev(kc8), dev(vc8)
+        binding.reshape_and_cache_fp8(dev(key), dev(val), gk, gv, dev(slots), ks, vs)
+        torch.cuda.synchronize()
+        rk, rv = oracle.reshape_and_cache_fp8(key, val, kc8, vc8, slots, ks, vs)
+        assert torch.equal(gk.cpu(), rk) and torch.equal(gv.cpu(), rv)
+        assert int(rk[0, 0, 0, 0]) == ck and int(rk[0, 0, 5, 0]) == 0x80 | ck
+        assert int(rv[1, 1, 3, 0]) == cv and int(rv[1, 1, 3, 15]) == 0x80 | cv
+    # the fused write of a decode step takes the same reading
+    c = W.make_case("fp8 scale reading", 316, "bf16", 8, 2, 64, 16, [5, 17, 40],
+                    new_positions=[4, 16, 39], extra_blocks=1)
+    c.new_key[:] = float(x[0])
+    c.new_value[:] = float(x[1])
+    c.new_key[1] = -c.new_key[1]
+    kc8, vc8 = fp8_pools(c, 0.3, 1.7)
+    say("fp8 scale reading, fused decode write")
+    _fp8_append_vs_oracle(c, 0.3, 1.7, kc8, vc8)

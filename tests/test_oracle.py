@@ -59,6 +59,12 @@ MUTATIONS = {
     "fp8_nan_saturates": ("    if (y != y)\n        return 0x7F;", "    if (y != y)\n        return 0x7E;"),
     "fp8_v_not_transposed": ("value_cache[page + (size_t)d * block_size + off] =",
                              "value_cache[page + (size_t)off * head_dim + d] ="),
+    "fp8_encode_divides": ("codes[i] = (unsigned char)e4m3_encode(x[i] * inv);",
+                           "codes[i] = (unsigned char)e4m3_encode(x[i] / scale);"),
+    "fp8_write_k_divides": ("(unsigned char)e4m3_encode(k * kinv);",
+                            "(unsigned char)e4m3_encode(k / k_scale);"),
+    "fp8_write_v_divides": ("(unsigned char)e4m3_encode(v * vinv);",
+                            "(unsigned char)e4m3_encode(v / v_scale);"),
     "fp8_subnormal_exponent": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
     "fp8_prefill_drops_diagonal": (
         "                                      pos + 1, num_kv_heads, h / group, block_size, head_dim,\n"
