@@ -616,6 +616,7 @@ def test_fp8_scale_reading_separating_values(dtype):
         key = torch.full((T, Hkv, D), float(xk)).to(tdt)
         val = torch.full((T, Hkv, D), float(xv)).to(tdt)
         key[1::2] = -key[1::2]
+        val[1::2] = -val[1::2]
         kc8 = torch.full((2, Hkv, B, D), 0x55, dtype=torch.uint8)
         vc8 = torch.full((2, Hkv, D, B), 0x55, dtype=torch.uint8)
         slots = torch.tensor([0, 5, 16, 31], dtype=torch.int64)
