@@ -165,6 +165,34 @@ pa_status pa_decode(void *out, const void *query, const void *key_cache,
                     size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that forbid hipMalloc,
+ * harnesses that forbid it): the same arguments, split, kernels and results
+ * as pa_decode, bit for bit, without the workspace arguments.
+ *
+ * The workspace lives in a static device array inside the library, one copy
+ * per GPU, of pa_decode_no_alloc_max_workspace() bytes (32 MiB), held from
+ * the first call on a device until the process ends.  The call allocates
+ * nothing.  A batch whose pa_decode_workspace_bytes() exceeds that size is
+ * rejected with PA_ERR_WORKSPACE before anything is enqueued.  The array is
+ * found for the current device (hipGetDevice), which must be the device of
+ * `stream`.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind (no call needs them cleared): calls that overlap on one
+ * GPU (on different streams, or from different threads without ordering)
+ * race and their outputs are undefined; order them on one stream.
+ */
+pa_status pa_decode_no_alloc(void *out, const void *query, const void *key_cache,
+                             const void *value_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, int32_t partition_size, float scale,
+                             int32_t dtype, void *stream);
+
+/* Bytes of the static workspace pa_decode_no_alloc uses on each GPU. */
+size_t pa_decode_no_alloc_max_workspace(void);
+
+/*
  * The two phases of pa_decode, callable on their own (same arguments; the
  * pair enqueued back to back on one stream is exactly pa_decode).
  * pa_decode_partitions writes the final output of every sequence that fits in

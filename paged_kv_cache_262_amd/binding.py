@@ -35,6 +35,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _i32, _i32, _f, _i32, _vp, _sz, _vp]),
+    "pa_decode_no_alloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i64, _i32, _i32, _f, _i32, _vp]),
+    "pa_decode_no_alloc_max_workspace": (_sz, []),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i64, _i32, _i32, _f, _i32, _vp, _sz, _vp]),
     "pa_decode_reduce": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -192,6 +195,19 @@ def decode(out, query, key_cache, value_cache, block_tables, context_lens, scale
                                           context_lens, max_context_len, partition_size, scale,
                                           workspace), _stream(stream)))
     return out
+
+
+def decode_no_alloc(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                    max_context_len, partition_size=0, stream=None):
+    """pa_decode with the library's static per-GPU workspace (no allocation)."""
+    args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                        max_context_len, partition_size, scale, None)[:-2]
+    _check(load().pa_decode_no_alloc(*args, _stream(stream)))
+    return out
+
+
+def decode_no_alloc_max_workspace() -> int:
+    return int(load().pa_decode_no_alloc_max_workspace())
 
 
 def decode_partitions(out, query, key_cache, value_cache, block_tables, context_lens, scale,

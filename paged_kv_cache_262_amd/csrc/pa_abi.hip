@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "pa.h"
@@ -338,6 +339,41 @@ pa_status debug_copy(const void *mapping, int32_t num_pairs, int64_t src_num_blo
     return PA_OK;
 }
 
+// ---- the decode workspace of pa_decode_no_alloc: a static device array ----
+//
+// For callers that cannot allocate (code under graph capture, serving loops
+// that forbid hipMalloc): the partial records and the unit scan of pa_decode
+// live in this file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it only names a stand-in): its device address is looked up once per
+// device with hipGetSymbolAddress and that address is what the kernels get.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's copy of `scratch`.
+pa_status scratch_for_current_device(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PA_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -463,6 +499,42 @@ pa_status pa_decode(void *out, const void *query, const void *key_cache,
     s = hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream), "decode_partitions");
     if (s != PA_OK) return s;
     return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
+}
+
+size_t pa_decode_no_alloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+pa_status pa_decode_no_alloc(void *out, const void *query, const void *key_cache,
+                             const void *value_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, int32_t partition_size, float scale,
+                             int32_t dtype, void *stream) {
+    // Every argument check of pa_decode first (no device call), with a
+    // stand-in workspace address, then the size of the plan's workspace.
+    DecodeSetup st;
+    pa_status s = setup_decode(st, out, query, key_cache, value_cache, block_tables,
+                               context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                               block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                               partition_size, scale, dtype, (void *)(uintptr_t)256,
+                               kNoAllocScratchBytes, true);
+    if (s != PA_OK) {
+        if (s == PA_ERR_WORKSPACE)
+            return fail(PA_ERR_WORKSPACE,
+                        "this decode needs %zu bytes of workspace; the static scratch holds %zu",
+                        pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                  block_size, max_context_len, partition_size),
+                        kNoAllocScratchBytes);
+        return s;
+    }
+    if (num_seqs == 0) return PA_OK;
+    void *ws = nullptr;
+    s = scratch_for_current_device(&ws);
+    if (s != PA_OK) return s;
+    return pa_decode(out, query, key_cache, value_cache, block_tables, context_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_context_len, partition_size, scale, dtype, ws,
+                     kNoAllocScratchBytes, stream);
 }
 
 pa_status pa_decode_append_partitions(void *out, const void *query, const void *new_key,

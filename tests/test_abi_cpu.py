@@ -185,3 +185,19 @@ def test_fp8_prefill_rejects(lib):
     assert f(*bad, 1.0, 1.0, None) == INVALID
     bad = list(args); bad[7] = 0                                    # no chunks: nothing to do
     assert f(*bad, 1.0, 1.0, None) == OK
+
+
+def test_no_alloc_decode_rejects_on_the_host(lib):
+    """pa_decode_no_alloc checks its arguments, and the size of the workspace
+    the plan needs against its static array, before any device call."""
+    f = lib.pa_decode_no_alloc
+    assert lib.pa_decode_no_alloc_max_workspace() == 32 << 20
+    args = [A, A, A, A, A, A, 8192, 8, 2, 128, 16, 3, 4, 40, 0, 0.1, 1, None]
+    assert f(*args) == WORKSPACE                      # ~34.6 MiB of records
+    assert "static scratch" in lib.pa_last_error().decode()
+    bad = list(args); bad[6] = 64; bad[1] = 0         # NULL query
+    assert f(*bad) == INVALID
+    bad = list(args); bad[6] = 64; bad[9] = 96        # head_dim not built
+    assert f(*bad) == UNSUPPORTED
+    bad = list(args); bad[6] = 0                      # no sequences: nothing to do
+    assert f(*bad) == OK
