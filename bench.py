@@ -22,6 +22,7 @@ bandwidth: algorithmic KV bytes of the step / step time.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -49,13 +50,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama8b_decode", choices=sorted(W.NAMED))
+    ap.add_argument("--workload", default=None, choices=sorted(W.NAMED),
+                    help="time only this workload (default: the Llama-3-8B-shaped decode as "
+                         "the headline, then every other workload and the ceilings)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default run: only the headline workload")
     ap.add_argument("--partition-size", type=int, default=0,
                     help="0: balanced split over waves (default); >0: fixed partitions")
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="minimum CPU time spent on the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="the oracle baseline repeats its full-workload run until this much "
+                         "time has passed")
+    ap.add_argument("--cpu-max-seconds", type=float, default=30.0,
+                    help="cap on the whole oracle baseline (all threads, then one thread)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     ap.add_argument("--op", default="attention",
@@ -74,6 +82,8 @@ def parse():
 # Sources each kernel is built from; the traffic figures in
 # profiles/hbm_traffic.txt are only reported while these are unchanged.
 KERNEL_SOURCES = {
+    "reshape_and_cache_kernel": ["reshape_and_cache.hip", "pa_common.h", "pa_internal.h"],
+    "reshape_and_cache_fp8_kernel": ["reshape_and_cache.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_fp8_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
@@ -83,24 +93,43 @@ KERNEL_SOURCES = {
 }
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
-    (scaled by a copy of known size), or None if not measured on these sources."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+def _source_digest(kernel: str):
+    if kernel not in KERNEL_SOURCES:
         return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "paged_kv_cache_262_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    digest = h.hexdigest()[:16]
+    return h.hexdigest()[:16]
+
+
+def _profile_value(table: str, kernel: str, workload: str):
+    """Column 4 of the row (kernel, workload, hash of the kernel's current
+    sources) of a table under profiles/, or None when no row matches."""
+    path = os.path.join(ROOT, "profiles", table)
+    digest = _source_digest(kernel)
+    if digest is None or not os.path.exists(path):
+        return None
     with open(path) as fh:
         for line in fh:
             parts = line.split()
-            if len(parts) >= 4 and not line.startswith("#") and parts[:3] == [kernel, workload,
-                                                                               digest]:
-                return int(parts[3])
+            if (len(parts) >= 4 and not line.startswith("#")
+                    and parts[:3] == [kernel, workload, digest]):
+                return float(parts[3])
     return None
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by a copy of known size), or None if not measured on these sources."""
+    v = _profile_value("hbm_traffic.txt", kernel, workload)
+    return None if v is None else int(v)
+
+
+def profiled_duration_ns(kernel: str, workload: str):
+    """Average launch duration from a rocprofv3 kernel trace of this workload
+    on the current sources, or None."""
+    return _profile_value("kernel_times.txt", kernel, workload)
 
 
 def fused_append(case) -> bool:
@@ -169,6 +198,23 @@ class Replica:
             self.cout = torch.empty_like(self.cq)
 
 
+METRICS = {
+    "llama8b_decode": METRIC,
+    "tiny_decode": "paged-attn decode KV GB/s + seq-tokens/s, tiny fp32 shape (4 seqs, d 64)",
+    "long_context_decode": "paged-attn decode KV GB/s (% of HBM peak) + seq-tokens/s, "
+                           "70B-shaped GQA, 8 seqs x 32K",
+    "prefix_sharing_decode": "paged-attn decode unique-KV GB/s (% of HBM peak), 128 seqs "
+                             "sharing a 1024-token prefix",
+    "mixed_chunked_prefill": "mixed chunked-prefill step: decode KV GB/s + prefill TFLOP/s "
+                             "(% of bf16 MFMA peak)",
+}
+# The other workloads the default run measures after the headline one.
+EXTRA_WORKLOADS = [("tiny_decode", False), ("long_context_decode", False),
+                   ("prefix_sharing_decode", False), ("mixed_chunked_prefill", False),
+                   ("llama8b_decode", True), ("long_context_decode", True),
+                   ("prefix_sharing_decode", True), ("mixed_chunked_prefill", True)]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,24 +227,67 @@ def main():
         sys.exit(1)
     binding.load()
     dev = torch.device("cuda:0")
-    case = W.NAMED[args.workload]()
+    full_run = args.workload is None
+    name = args.workload or "llama8b_decode"
+    case = W.NAMED[name]()
     if args.op == "block_manager":
         return run_block_manager(args, case)
     if args.op != "attention":
         return run_copy(args, case, dev)
-    S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
-                        case.block_size)
     fp8 = args.kv == "fp8"
     if fp8 and (case.dtype != "bf16" or args.partition_size):
         print("--kv fp8 runs bf16 workloads with the balanced split", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib, dev)
+    result, reps = measure(case, dev, fp8, args.partition_size, args.steps, args.warmup,
+                           args.replicas)
+    del reps
+    torch.cuda.empty_cache()
+    ceilings = None
+    if full_run and not args.no_extra:
+        result["workloads"] = {}
+        for wname, wfp8 in EXTRA_WORKLOADS:
+            wcase = case if wname == name else W.NAMED[wname]()
+            r, wreps = measure(wcase, dev, wfp8, 0, args.steps, args.warmup, args.replicas)
+            del wreps
+            torch.cuda.empty_cache()
+            result["workloads"][wname + ("_fp8" if wfp8 else "")] = summary(r)
+        ceilings = measure_ceilings(dev, result["roofline"]["algorithmic_bytes_per_launch"])
+        result["ceilings"] = ceilings
+        attach_attainable(result, ceilings)
+        for r in result["workloads"].values():
+            attach_attainable(r, ceilings)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, fp8, args.cpu_seconds,
+                                              args.cpu_max_seconds, result["_kv_bytes"])
+    result.pop("_kv_bytes", None)
+    print(json.dumps(result), flush=True)
+
+
+def copy_probe(mib, dev):
+    """One plain device copy of known size (the counter calibration)."""
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
+
+
+def measure(case, dev, fp8, P, steps, warmup, replicas):
+    """Times `steps` steps of the hot path on one workload (after `warmup`
+    untimed ones), then the same steps again with an event around each kernel
+    for the per-kernel breakdown.  Returns (result dict, device replicas)."""
+    S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                        case.block_size)
+    label = case.name + (" (FP8 e4m3 KV cache)" if fp8 else "")
+    print(f"workload {label}: setting up", file=sys.stderr, flush=True)
     eb = 1 if fp8 else case.key_cache.element_size()  # bytes per cached element
     lens = case.context_lens.tolist()
     maxL = case.max_context_len
-    P = args.partition_size  # 0: balanced split of all units over the waves
-    reps = [Replica(case, dev, fp8)]
-    for _ in range(1, max(1, args.replicas)):
-        reps.append(Replica(case, dev, fp8))
+    reps = [Replica(case, dev, fp8) for _ in range(max(1, replicas))]
     ws = binding.make_workspace(reps[0].q, reps[0].kc, maxL, P)
     stream = torch.cuda.current_stream()
 
@@ -221,21 +310,27 @@ def main():
     maxq = max((n for n, _ in chunks), default=0)
 
     ev = {k: [] for k in ("cw0", "cw1", "dp0", "dp1", "dr1", "pf0", "pf1")}
-
     fused = fused_append(case)
+    # Events of the per-kernel pass, created before it starts.
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(5 * steps)]
+
+    def mark(key):
+        e = pool.pop()
+        e.record(stream)
+        ev[key].append(e)
+        return e
 
     def step(i, record):
         r = reps[i % len(reps)]
         if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw0"].append(e)
+            mark("cw0")
         if T and fp8 and not fused:
             binding.reshape_and_cache_fp8(r.nk, r.nv, r.kc, r.vc, r.slots, FP8_K_SCALE,
                                           FP8_V_SCALE, stream=stream)
         elif T and not fused:
             binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
         if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["cw1"].append(e)
-            ev["dp0"].append(e)
+            ev["dp0"].append(mark("cw1"))
         if fp8 and fused:
             binding.decode_fp8_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
                                                  r.lens, case.scale, maxL, FP8_K_SCALE,
@@ -250,14 +345,14 @@ def main():
             binding.decode_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL, P,
                                       ws, stream=stream)
         if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dp1"].append(e)
+            mark("dp1")
         binding.decode_reduce(r.out, r.lens, Hkv, B, case.max_blocks_per_seq, maxL, P, ws,
                               stream=stream)
         if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["dr1"].append(e)
+            e = mark("dr1")
         if chunks:
             if record:
-                ev["pf0"].append(ev["dr1"][-1])
+                ev["pf0"].append(e)
             if fp8:
                 binding.prefill_chunk_fp8(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens,
                                           case.scale, maxq, FP8_K_SCALE, FP8_V_SCALE,
@@ -266,66 +361,65 @@ def main():
                 binding.prefill_chunk(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens, case.scale,
                                       maxq, stream=stream)
             if record:
-                e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["pf1"].append(e)
+                mark("pf1")
 
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        print(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written",
-              file=sys.stderr, flush=True)
-        del a, b
-
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, False)
     torch.cuda.synchronize()
-    print(f"warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"warmup done ({warmup} steps)", file=sys.stderr, flush=True)
 
     # The timed steps carry no events between kernels; a second pass of the
-    # same steps records one event around each kernel for the breakdown.
+    # same steps records one event around each kernel for the breakdown.  The
+    # garbage collector is off meanwhile: a collection that stalls the host
+    # long enough to drain the queue would show up inside one interval.
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start = torch.cuda.Event(enable_timing=True); e_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, False)
     e_end = torch.cuda.Event(enable_timing=True); e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e_start.elapsed_time(e_end) / args.steps
-    print(f"timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
+    ms_step = e_start.elapsed_time(e_end) / steps
+    print(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, True)
     torch.cuda.synchronize()
+    gc.enable()
     print("per-kernel pass done", file=sys.stderr, flush=True)
 
-    def avg_ms(a, b):
-        xs = [x.elapsed_time(y) for x, y in zip(ev[a], ev[b])]
-        return sum(xs) / len(xs) if xs else 0.0
+    medians = {}
 
-    t_cw = avg_ms("cw0", "cw1")
+    def avg_ms(a, b):
+        xs = sorted(x.elapsed_time(y) for x, y in zip(ev[a], ev[b]))
+        if not xs:
+            return None
+        medians[a + b] = xs[len(xs) // 2]
+        return sum(xs) / len(xs)
+
+    t_cw = avg_ms("cw0", "cw1") if T and not fused else None
     t_dp = avg_ms("dp0", "dp1")
     t_dr = avg_ms("dp1", "dr1")
-    t_pf = avg_ms("pf0", "pf1") if chunks else 0.0
+    t_pf = avg_ms("pf0", "pf1") if chunks else None
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    wl = case.name + ("_fp8" if fp8 else "")
     # bf16 uses the matrix-core variant of the balanced split.
     dp_kernel = ("decode_stream_fp8_kernel" if fp8 else
                  "decode_partition_kernel" if P != 0 or S > 8192 else
                  "decode_stream_mma_kernel" if case.dtype == "bf16" else "decode_stream_kernel")
     # The fused step's decode kernel also moves the new tokens' rows.
     dp_bytes = dec_bytes + (cw_bytes if fused else 0)
-    dp_gbs = dp_bytes / (t_dp * 1e-3) / 1e9
     result = {
-        "metric": METRIC,
+        "metric": METRICS[case.name] + (", FP8 e4m3 KV cache" if fp8 else ""),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -333,7 +427,7 @@ def main():
         "dtype": "fp8_e4m3 kv, bf16 q" if fp8 else case.dtype,
         "data": "synthetic",
         "config": {
-            "workload": case.name + (" (FP8 e4m3 KV cache)" if fp8 else ""),
+            "workload": label,
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
@@ -347,39 +441,130 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_tokens_per_s": round(sum(lens) / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(S / (ms_step * 1e-3), 1),
-        "kernels_ms": {"reshape_and_cache": round(t_cw, 5), "decode_partition": round(t_dp, 5),
-                       "decode_reduce": round(t_dr, 5), "prefill_chunk": round(t_pf, 5)},
-        "roofline": {
-            "kernel": dp_kernel,
-            "bound": "hbm",
-            "achieved": round(dp_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(dp_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dp_kernel, case.name + ("_fp8" if fp8 else "")),
-            "algorithmic_bytes_per_launch": dp_bytes,
-        },
+        "kernels_ms": {"reshape_and_cache": "fused" if fused else _r(t_cw),
+                       "decode_partition": _r(t_dp), "decode_reduce": _r(t_dr),
+                       "prefill_chunk": _r(t_pf)},
+        "roofline": roofline(dp_kernel, wl, "hbm", dp_bytes, t_dp, HBM_PEAK_GBS,
+                             medians["dp0dp1"]),
+        "_kv_bytes": kv_bytes,
     }
     if chunks:
-        tf = pf_flops / (t_pf * 1e-3) / 1e12
         pf_kernel = "prefill_chunk_fp8_kernel" if fp8 else "prefill_chunk_kernel"
-        result["prefill_roofline"] = {"kernel": pf_kernel, "bound": "mfma",
-                                      "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                                      "unit": "TFLOP/s",
-                                      "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                      "traffic": measured_traffic(
-                                          pf_kernel, case.name + ("_fp8" if fp8 else "")),
-                                      "algorithmic_flops_per_launch": pf_flops,
-                                      "query_tokens_per_s": round(
-                                          sum(n for n, _ in chunks) / (t_pf * 1e-3), 1)}
-    if T and not fused:
-        result["cache_write"] = {"ms": round(t_cw, 5), "bytes": cw_bytes,
-                                 "GB/s": round(cw_bytes / (t_cw * 1e-3) / 1e9, 1)}
+        pr = roofline(pf_kernel, wl, "mfma", pf_flops, t_pf, BF16_MFMA_PEAK_TFLOPS,
+                      medians["pf0pf1"])
+        pr["query_tokens_per_s"] = round(sum(n for n, _ in chunks) / (t_pf * 1e-3), 1)
+        result["prefill_roofline"] = pr
+    if t_cw is not None:
+        cw_kernel = "reshape_and_cache_fp8_kernel" if fp8 else "reshape_and_cache_kernel"
+        cw = roofline(cw_kernel, wl, "hbm", cw_bytes, t_cw, HBM_PEAK_GBS, medians["cw0cw1"])
+        cw["GB/s"] = cw["achieved"]
+        result["cache_write"] = cw
+    return result, reps
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (cpu_baseline_fp8(case, reps[0], args.cpu_seconds, kv_bytes)
-                                  if fp8 else cpu_baseline(case, args.cpu_seconds, kv_bytes))
-    print(json.dumps(result), flush=True)
+
+def _r(x, nd=5):
+    return None if x is None else round(x, nd)
+
+
+def roofline(kernel, workload, bound, work, ms, peak, median_ms):
+    """Roofline entry of one kernel: `work` algorithmic bytes (hbm) or flops
+    (mfma) per launch over its event-timed average `ms`; beside it the same
+    work over the rocprofv3 kernel-trace average committed for these sources,
+    when there is one."""
+    scale = 1e9 if bound == "hbm" else 1e12
+    achieved = work / (ms * 1e-3) / scale
+    r = {"kernel": kernel, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+         "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": round(achieved / peak, 4),
+         "timer": "HIP events around each launch on its stream",
+         "traffic": measured_traffic(kernel, workload),
+         ("algorithmic_bytes_per_launch" if bound == "hbm"
+          else "algorithmic_flops_per_launch"): work,
+         "event_us": round(ms * 1e3, 2), "event_median_us": round(median_ms * 1e3, 2)}
+    prof_ns = profiled_duration_ns(kernel, workload)
+    if prof_ns is not None:
+        a = work / (prof_ns * 1e-9) / scale
+        r["rocprof_us"] = round(prof_ns / 1e3, 2)
+        r["rocprof_frac"] = round(a / peak, 4)
+    else:
+        r["rocprof_us"] = r["rocprof_frac"] = None
+    return r
+
+
+def summary(r):
+    """The per-workload entry of the default run's line."""
+    keys = ("metric", "value", "unit", "ms_per_step", "hbm_frac", "seq_tokens_per_s",
+            "kernels_ms", "roofline", "prefill_roofline", "cache_write")
+    out = {k: r[k] for k in keys if k in r}
+    out["step_us"] = round(r["ms_per_step"] * 1e3, 2)
+    out["workload"] = r["config"]["workload"]
+    return out
+
+
+def measure_ceilings(dev, decode_bytes):
+    """Attainable ceilings measured next to the kernels: a streaming read of
+    2 x 1 GiB and of two buffers of the 8B decode's algorithmic size
+    (alternated, so the last-level cache cannot serve one read from the
+    previous one), and the bf16 matrix-core probe."""
+    stream = torch.cuda.current_stream()
+    sink = binding.probe_sink(dev)
+
+    def time_reads(nbytes, launches):
+        nbytes = -(-nbytes // 16) * 16
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(2)]
+        for i in range(4):
+            binding.probe_stream_read(bufs[i % 2], sink, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+        for i in range(launches):
+            binding.probe_stream_read(bufs[i % 2], sink, stream=stream)
+        e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        del bufs
+        return nbytes, ms
+
+    nb, ms = time_reads(1 << 30, 20)
+    big = nb / (ms * 1e-3) / 1e9
+    nb2, ms2 = time_reads(decode_bytes, 40)
+    fit = nb2 / (ms2 * 1e-3) / 1e9
+    torch.cuda.empty_cache()
+
+    # About 1 ms per launch; 20 launches bring the clock up before the 10 timed.
+    iters = 5000
+    for _ in range(20):
+        binding.probe_mfma_bf16(sink, iters, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+    flops = 0.0
+    for _ in range(10):
+        flops += binding.probe_mfma_bf16(sink, iters, stream=stream)
+    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+    torch.cuda.synchronize()
+    tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    print(f"ceilings: read {big:.0f} GB/s (1 GiB), {fit:.0f} GB/s ({nb2} B); "
+          f"bf16 MFMA {tf:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    return {
+        "stream_read": {"op": "pa_probe_stream_read", "GB/s": round(big, 1),
+                        "frac_of_peak": round(big / HBM_PEAK_GBS, 4), "bytes": nb,
+                        "peak": HBM_PEAK_GBS},
+        "stream_read_decode_size": {"op": "pa_probe_stream_read", "GB/s": round(fit, 1),
+                                    "bytes": nb2, "us": round(ms2 * 1e3, 2),
+                                    "frac_of_peak": round(fit / HBM_PEAK_GBS, 4)},
+        "mfma_bf16": {"op": "pa_probe_mfma_bf16", "TFLOP/s": round(tf, 1),
+                      "frac_of_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                      "peak": BF16_MFMA_PEAK_TFLOPS},
+    }
+
+
+def attach_attainable(r, ceilings):
+    """Each roofline's achieved rate as a fraction of the measured ceiling."""
+    for key in ("roofline", "cache_write"):
+        if r.get(key):
+            r[key]["frac_of_attainable"] = round(
+                r[key]["achieved"] / ceilings["stream_read"]["GB/s"], 4)
+    if r.get("prefill_roofline"):
+        r["prefill_roofline"]["frac_of_attainable"] = round(
+            r["prefill_roofline"]["achieved"] / ceilings["mfma_bf16"]["TFLOP/s"], 4)
 
 
 def run_block_manager(args, case):
@@ -550,48 +735,116 @@ def run_copy(args, case, dev):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(case, min_seconds, kv_bytes):
-    """The fp64 oracle (test infrastructure, as it stands) on the same decode
-    workload, on this host's cores, repeated until min_seconds have passed."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp():
+    """The OpenMP runtime the oracle library is linked against."""
+    import ctypes
+    try:
+        return ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+
+
+def cpu_baseline(case, fp8, min_seconds, max_seconds, kv_bytes):
+    """The fp64 oracle (test infrastructure, as it stands) on the same step:
+    the cache write of the new tokens, decode over every sequence and, for the
+    chunked-prefill workload, the prefill chunks.  First on all of this host's
+    threads, repeated until min_seconds have passed; then on one thread over a
+    sample of the sequences, scaled by the sample's share of the KV bytes.
+    Neither part runs past max_seconds in total."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    kc, vc = (oracle.reshape_and_cache(case.new_key, case.new_value, case.key_cache,
-                                       case.value_cache, case.slot_mapping)
-              if case.slot_mapping.numel() else (case.key_cache, case.value_cache))
+    t_begin = time.perf_counter()
+    omp = _omp()
+    threads = omp.omp_get_max_threads() if omp else int(os.environ.get("OMP_NUM_THREADS", 1))
+    if fp8:
+        # Seeded random e4m3 codes (NaN codes excluded) in the pool shapes: the
+        # oracle's time does not depend on the values, and encoding the whole
+        # pools with its table search would take minutes.  Untimed.
+        g = torch.Generator().manual_seed(0)
+        NB, Hkv_, B_, D_ = case.key_cache.shape
+        kc0 = torch.randint(0, 256, (NB, Hkv_, B_, D_), dtype=torch.uint8, generator=g)
+        vc0 = torch.randint(0, 256, (NB, Hkv_, D_, B_), dtype=torch.uint8, generator=g)
+        for t in (kc0, vc0):
+            t[(t & 0x7F) == 0x7F] -= 1
+
+        def dec(q, bt, lens):
+            return oracle.decode_fp8(q, kc, vc, bt, lens, case.scale, FP8_K_SCALE, FP8_V_SCALE)
+    else:
+        kc0, vc0 = case.key_cache, case.value_cache
+
+        def dec(q, bt, lens):
+            return oracle.decode(q, kc, vc, bt, lens, case.scale)
+    kc, vc = kc0, vc0
+
+    def full_step():
+        nonlocal kc, vc
+        if case.slot_mapping.numel():
+            if fp8:
+                kc, vc = oracle.reshape_and_cache_fp8(case.new_key, case.new_value, kc0, vc0,
+                                                      case.slot_mapping, FP8_K_SCALE, FP8_V_SCALE)
+            else:
+                kc, vc = oracle.reshape_and_cache(case.new_key, case.new_value, kc0, vc0,
+                                                  case.slot_mapping)
+        dec(case.query, case.block_tables, case.context_lens)
+        if case.num_chunks:
+            args = (case.chunk_query, kc, vc, case.chunk_block_tables, case.chunk_cu_query_lens,
+                    case.chunk_context_lens, case.scale)
+            if fp8:
+                oracle.prefill_fp8(*args, FP8_K_SCALE, FP8_V_SCALE)
+            else:
+                oracle.prefill(*args)
+
+    budget = max_seconds * 0.6
     runs, t = 0, 0.0
-    while t < min_seconds or runs == 0:
+    while runs == 0 or (t < min_seconds and t + t / runs < budget):
         t0 = time.perf_counter()
-        oracle.decode(case.query, kc, vc, case.block_tables, case.context_lens, case.scale)
+        full_step()
         t += time.perf_counter() - t0
         runs += 1
     per = t / runs
-    return {"value": round(kv_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full {case.name} decode (all {case.num_seqs} seqs x "
-                      f"{case.num_q_heads} q heads, fp64), {runs} runs, "
-                      f"{per * 1e3:.1f} ms per run"}
-
-
-def cpu_baseline_fp8(case, rep, min_seconds, kv_bytes):
-    """The fp64 oracle's decode over the same FP8 pools (copied to the host),
-    on this host's cores, repeated until min_seconds have passed."""
-    import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    kc, vc = rep.kc.cpu(), rep.vc.cpu()
-    runs, t = 0, 0.0
-    while t < min_seconds or runs == 0:
+    what = "cache write + decode" + (" + prefill chunks" if case.num_chunks else "")
+    out = {"value": round(kv_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "cpu_model": _cpu_model(),
+           "sample": f"full {case.name} step ({what}; all {case.num_seqs} seqs x "
+                     f"{case.num_q_heads} q heads, fp64{', FP8 pools of random codes' if fp8 else ''}), "
+                     f"{runs} runs, {per * 1e3:.1f} ms per run on {threads} threads"}
+    # One thread, on the first sequences: as many as fit the remaining time
+    # at the measured rate (a thread is at most `threads` times slower).
+    left = max(0.5, max_seconds - (time.perf_counter() - t_begin))
+    lens = case.context_lens.tolist()
+    n = 1
+    est = per * threads / max(1, sum(lens))  # seconds per context token on one thread
+    while n < len(lens) and est * sum(lens[:n + 1]) < min(left * 0.8, min_seconds):
+        n += 1
+    if omp is not None:
+        omp.omp_set_num_threads(1)
+    try:
         t0 = time.perf_counter()
-        oracle.decode_fp8(case.query, kc, vc, case.block_tables, case.context_lens, case.scale,
-                          FP8_K_SCALE, FP8_V_SCALE)
-        t += time.perf_counter() - t0
-        runs += 1
-    per = t / runs
-    return {"value": round(kv_bytes / per / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full {case.name} decode over the FP8 pools (all {case.num_seqs} seqs x "
-                      f"{case.num_q_heads} q heads, fp64), {runs} runs, "
-                      f"{per * 1e3:.1f} ms per run"}
+        dec(case.query[:n].contiguous(), case.block_tables[:n].contiguous(),
+            case.context_lens[:n].contiguous())
+        t1 = time.perf_counter() - t0
+    finally:
+        if omp is not None:
+            omp.omp_set_num_threads(threads)
+    Hkv, D = case.num_kv_heads, case.head_dim
+    eb = 1 if fp8 else case.key_cache.element_size()
+    sample_bytes = sum(lens[:n]) * acct.kv_bytes_per_token(1, Hkv, D, eb)
+    out["one_thread"] = {"value": round(sample_bytes / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "sample": f"decode of the first {n} of {len(lens)} sequences "
+                                   f"({sum(lens[:n])} context tokens), {t1:.2f} s",
+                         "enforced": omp is not None}
+    out["seconds"] = round(time.perf_counter() - t_begin, 2)
+    return out
 
 
 if __name__ == "__main__":

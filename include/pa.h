@@ -546,6 +546,31 @@ pa_status pa_bm_block_tables(const pa_block_manager *bm, const int64_t *seq_ids,
 /* Pool statistics; internal fragmentation = 1 - seq_tokens / seq_slots. */
 pa_status pa_bm_get_stats(const pa_block_manager *bm, pa_bm_stats *stats);
 
+/*
+ * Ceiling probes -- the attainable rates the attention kernels are measured
+ * against (the pages report the decode kernel as bound by memory bandwidth:
+ * "vLLM High-Performance Inference Engine: PagedAttention Principles and
+ * Deployment Guide", section "PagedAttention Architecture Deep Dive").  They
+ * compute nothing of the method.
+ *
+ * pa_probe_stream_read: reads bytes (a positive multiple of 16) of device
+ * memory buf once with 16-byte loads spread over the whole chip, and writes
+ * pa_probe_sink_words() 32-bit words to sink (device memory, caller-owned),
+ * so that the read cannot be dropped.  Bytes / time is the streaming read
+ * rate.  buf must be 16-byte aligned, sink 4-byte aligned.
+ *
+ * pa_probe_mfma_bf16: every SIMD issues iters (>= 1) rounds of 4 independent
+ * 32x32x16 bf16 matrix products on register operands and writes
+ * pa_probe_sink_words() floats to sink; *flops (host, optional) receives the
+ * flops the launch performs.  Flops / time is the sustained dense bf16 rate.
+ *
+ * Both are asynchronous on stream; errors: PA_ERR_INVALID_ARG (bad size,
+ * null or misaligned pointer, pointer the device cannot address), PA_ERR_HIP.
+ */
+int64_t pa_probe_sink_words(void);
+pa_status pa_probe_stream_read(const void *buf, int64_t bytes, void *sink, void *stream);
+pa_status pa_probe_mfma_bf16(void *sink, int32_t iters, double *flops, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

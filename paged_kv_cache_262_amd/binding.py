@@ -50,6 +50,9 @@ SIGNATURES = {
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
+    "pa_probe_sink_words": (_i64, []),
+    "pa_probe_stream_read": (_i32, [_vp, _i64, _vp, _vp]),
+    "pa_probe_mfma_bf16": (_i32, [_vp, _i32, ctypes.POINTER(ctypes.c_double), _vp]),
     "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64,
                                         _i32, _f, _f, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -411,6 +414,33 @@ def copy_blocks(src_key_cache, src_value_cache, dst_key_cache, dst_value_cache, 
         src_key_cache.data_ptr(), src_value_cache.data_ptr(), dst_key_cache.data_ptr(),
         dst_value_cache.data_ptr(), block_mapping.data_ptr(), block_mapping.shape[0],
         src_key_cache.shape[0], dst_key_cache.shape[0], block_bytes, _stream(stream)))
+
+
+def probe_sink(device=None) -> torch.Tensor:
+    """A device buffer large enough for either probe's sink."""
+    return torch.empty(int(load().pa_probe_sink_words()), dtype=torch.int32,
+                       device=device or "cuda")
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read every byte of buf once (a streaming-read ceiling); buf is a
+    contiguous device tensor whose size is a multiple of 16 bytes."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if sink.numel() * sink.element_size() < 4 * int(load().pa_probe_sink_words()):
+        raise ValueError("sink is too small")
+    _check(load().pa_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                       sink.data_ptr(), _stream(stream)))
+
+
+def probe_mfma_bf16(sink: torch.Tensor, iters: int, stream=None) -> float:
+    """Launch the bf16 matrix-core probe; returns the flops it performs."""
+    if sink.numel() * sink.element_size() < 4 * int(load().pa_probe_sink_words()):
+        raise ValueError("sink is too small")
+    flops = ctypes.c_double(0.0)
+    _check(load().pa_probe_mfma_bf16(sink.data_ptr(), int(iters), ctypes.byref(flops),
+                                     _stream(stream)))
+    return flops.value
 
 
 class _BmStats(ctypes.Structure):

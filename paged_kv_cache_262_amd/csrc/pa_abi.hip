@@ -12,6 +12,7 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_probes.h"
 
 namespace {
 
@@ -859,6 +860,37 @@ pa_status pa_copy_blocks(const void *src_key_cache, const void *src_value_cache,
                                              (const int64_t *)dev[4], num_pairs, src_num_blocks,
                                              dst_num_blocks, block_bytes, (hipStream_t)stream),
                       "copy_blocks");
+}
+
+int64_t pa_probe_sink_words(void) {
+    const int g = pa::probe_read_grid() > pa::probe_mfma_grid() ? pa::probe_read_grid()
+                                                                 : pa::probe_mfma_grid();
+    return (int64_t)g * 256;
+}
+
+pa_status pa_probe_stream_read(const void *buf, int64_t bytes, void *sink, void *stream) {
+    if (bytes <= 0 || bytes % 16)
+        return fail(PA_ERR_INVALID_ARG, "bytes %lld is not a positive multiple of 16",
+                    (long long)bytes);
+    CHECK_PTR(buf, 16);
+    CHECK_PTR(sink, 4);
+    const void *dbuf, *dsink;
+    if (!device_view(buf, &dbuf) || !device_view(sink, &dsink))
+        return fail(PA_ERR_INVALID_ARG, "probe buffers must be memory the device can address");
+    return hip_status(pa::launch_probe_stream_read(dbuf, (size_t)bytes, (void *)dsink,
+                                                   (hipStream_t)stream),
+                      "probe_stream_read");
+}
+
+pa_status pa_probe_mfma_bf16(void *sink, int32_t iters, double *flops, void *stream) {
+    if (iters < 1) return fail(PA_ERR_INVALID_ARG, "iters must be >= 1");
+    CHECK_PTR(sink, 4);
+    const void *dsink;
+    if (!device_view(sink, &dsink))
+        return fail(PA_ERR_INVALID_ARG, "sink must be memory the device can address");
+    if (flops) *flops = pa::probe_mfma_flops(iters);
+    return hip_status(pa::launch_probe_mfma_bf16((void *)dsink, iters, (hipStream_t)stream),
+                      "probe_mfma_bf16");
 }
 
 }  // extern "C"

@@ -201,3 +201,15 @@ def test_no_alloc_decode_rejects_on_the_host(lib):
     assert f(*bad) == UNSUPPORTED
     bad = list(args); bad[6] = 0                      # no sequences: nothing to do
     assert f(*bad) == OK
+
+
+def test_probes_reject_bad_arguments_on_the_host(lib):
+    # checked before any device call
+    assert lib.pa_probe_sink_words() >= 4096 * 256
+    assert lib.pa_probe_stream_read(None, 16, None, None) == 1
+    assert lib.pa_probe_stream_read(None, 0, None, None) == 1
+    assert lib.pa_probe_stream_read(None, 24, None, None) == 1
+    assert b"multiple of 16" in lib.pa_last_error()
+    assert lib.pa_probe_mfma_bf16(None, 0, None, None) == 1
+    assert b"iters" in lib.pa_last_error()
+    assert lib.pa_probe_mfma_bf16(None, 5, None, None) == 1
