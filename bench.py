@@ -73,6 +73,9 @@ def parse():
                          "pa_copy_blocks on the workload's pool")
     ap.add_argument("--copy-seqs", type=int, default=8,
                     help="sequences whose blocks a copy op moves")
+    ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
+                    help="chunked-prefill workloads: 2 runs decode and prefill on two streams "
+                         "of equal priority (and also times the serial step)")
     ap.add_argument("--kv", default="native", choices=["native", "fp8"],
                     help="native: pools in the workload's dtype (default); fp8: e4m3 pools "
                          "written by pa_reshape_and_cache_fp8, decode by pa_decode_fp8")
@@ -87,6 +90,7 @@ KERNEL_SOURCES = {
     "decode_stream_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_fp8_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
+    "decode_stream_reduce_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
     "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
     "prefill_chunk_fp8_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
@@ -147,6 +151,22 @@ def fused_append(case) -> bool:
     return want == case.slot_mapping.tolist()
 
 
+def split_mixed(case) -> bool:
+    """A chunked-prefill step whose first num_seqs new tokens are one per
+    decode sequence at position L - 1 (the rest are the chunks' own tokens):
+    the decode tokens can then be written inside the decode pass and the
+    chunk tokens by a cache write on the prefill's stream."""
+    if not case.num_chunks or case.slot_mapping.numel() < case.num_seqs:
+        return False
+    B = case.block_size
+    lens = case.context_lens.tolist()
+    if min(lens) <= 0:
+        return False
+    bt = case.block_tables
+    want = [int(bt[s, (L - 1) // B]) * B + (L - 1) % B for s, L in enumerate(lens)]
+    return want == case.slot_mapping[:case.num_seqs].tolist()
+
+
 # Per-pool scales of the FP8 benchmark pools: N(0, 1) data over 1/32 spans
 # +-14 before saturation.
 FP8_K_SCALE = FP8_V_SCALE = 1.0 / 32
@@ -186,10 +206,14 @@ class Replica:
         self.nv = case.new_value.to(dev)
         self.slots = case.slot_mapping.to(dev)
         self.out = torch.empty_like(self.q)
-        if fused_append(case):
-            S, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
-            self.nk_seq = case.new_key.reshape(S, Hkv, D).to(dev)
-            self.nv_seq = case.new_value.reshape(S, Hkv, D).to(dev)
+        S = case.num_seqs
+        if fused_append(case) or split_mixed(case):
+            self.nk_seq = case.new_key[:S].contiguous().to(dev)
+            self.nv_seq = case.new_value[:S].contiguous().to(dev)
+        if split_mixed(case):
+            self.nk_chunk = case.new_key[S:].contiguous().to(dev)
+            self.nv_chunk = case.new_value[S:].contiguous().to(dev)
+            self.slots_chunk = case.slot_mapping[S:].contiguous().to(dev)
         if case.num_chunks:
             self.cq = case.chunk_query.to(dev)
             self.cbt = case.chunk_block_tables.to(dev)
@@ -241,7 +265,7 @@ def main():
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, dev)
     result, reps = measure(case, dev, fp8, args.partition_size, args.steps, args.warmup,
-                           args.replicas)
+                           args.replicas, args.streams)
     del reps
     torch.cuda.empty_cache()
     ceilings = None
@@ -276,7 +300,7 @@ def copy_probe(mib, dev):
     print(f"copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
-def measure(case, dev, fp8, P, steps, warmup, replicas):
+def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
     """Times `steps` steps of the hot path on one workload (after `warmup`
     untimed ones), then the same steps again with an event around each kernel
     for the per-kernel breakdown.  Returns (result dict, device replicas)."""
@@ -363,8 +387,57 @@ def measure(case, dev, fp8, P, steps, warmup, replicas):
             if record:
                 mark("pf1")
 
+    # streams == 2: a chunked-prefill step whose decode tokens can be written
+    # inside the decode pass runs as two streams of equal priority: decode
+    # (with those writes) and its reduce on the current stream; the cache
+    # write of the chunk tokens and the prefill on a second one.  The two meet
+    # at the end of every step.  (The kernels cannot share a CU, so this is
+    # slower than the serial step; it is kept to measure that.)
+    overlap = streams == 2 and bool(chunks) and split_mixed(case)
+    side = torch.cuda.Stream(device=dev) if overlap else None
+    forks = [torch.cuda.Event() for _ in range(2)]
+    joins = [torch.cuda.Event() for _ in range(2)]
+
+    def overlapped_step(i):
+        r = reps[i % len(reps)]
+        fork, join = forks[i % 2], joins[i % 2]
+        fork.record(stream)
+        side.wait_event(fork)
+        if fp8:
+            binding.decode_fp8_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
+                                                 r.lens, case.scale, maxL, FP8_K_SCALE,
+                                                 FP8_V_SCALE, ws, stream=stream)
+            binding.reshape_and_cache_fp8(r.nk_chunk, r.nv_chunk, r.kc, r.vc, r.slots_chunk,
+                                          FP8_K_SCALE, FP8_V_SCALE, stream=side)
+            binding.prefill_chunk_fp8(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens,
+                                      case.scale, maxq, FP8_K_SCALE, FP8_V_SCALE, stream=side)
+        else:
+            binding.decode_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
+                                             r.lens, case.scale, maxL, P, ws, stream=stream)
+            binding.reshape_and_cache(r.nk_chunk, r.nv_chunk, r.kc, r.vc, r.slots_chunk,
+                                      stream=side)
+            binding.prefill_chunk(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens, case.scale,
+                                  maxq, stream=side)
+        join.record(side)
+        binding.decode_reduce(r.out, r.lens, Hkv, B, case.max_blocks_per_seq, maxL, P, ws,
+                              stream=stream)
+        stream.wait_event(join)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, time.perf_counter() - t0
+
+    run_step = overlapped_step if overlap else (lambda i: step(i, False))
     for i in range(warmup):
-        step(i, False)
+        run_step(i)
+        if overlap:
+            step(i, False)
     torch.cuda.synchronize()
     print(f"warmup done ({warmup} steps)", file=sys.stderr, flush=True)
 
@@ -374,17 +447,10 @@ def measure(case, dev, fp8, P, steps, warmup, replicas):
     # long enough to drain the queue would show up inside one interval.
     gc.collect()
     gc.disable()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_start = torch.cuda.Event(enable_timing=True); e_start.record(stream)
-    for i in range(steps):
-        step(i, False)
-    e_end = torch.cuda.Event(enable_timing=True); e_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e_start.elapsed_time(e_end) / steps
+    ms_step, wall = timed(run_step, steps)
     print(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
+    serial_ms = timed(lambda i: step(i, False), steps)[0] if overlap else None
     for i in range(steps):
         step(i, True)
     torch.cuda.synchronize()
@@ -437,10 +503,13 @@ def measure(case, dev, fp8, P, steps, warmup, replicas):
                             else "pa_reshape_and_cache" if T else "none"),
             "replicas": len(reps),
             "prefill_chunks": chunks,
+            "streams": ("2 of equal priority: decode with its tokens' cache write + reduce; "
+                        "the chunk tokens' cache write + prefill" if overlap else "1"),
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "seq_tokens_per_s": round(sum(lens) / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(S / (ms_step * 1e-3), 1),
+        "serial_ms_per_step": _r(serial_ms),
         "kernels_ms": {"reshape_and_cache": "fused" if fused else _r(t_cw),
                        "decode_partition": _r(t_dp), "decode_reduce": _r(t_dr),
                        "prefill_chunk": _r(t_pf)},
@@ -492,8 +561,8 @@ def roofline(kernel, workload, bound, work, ms, peak, median_ms):
 
 def summary(r):
     """The per-workload entry of the default run's line."""
-    keys = ("metric", "value", "unit", "ms_per_step", "hbm_frac", "seq_tokens_per_s",
-            "kernels_ms", "roofline", "prefill_roofline", "cache_write")
+    keys = ("metric", "value", "unit", "ms_per_step", "serial_ms_per_step", "hbm_frac",
+            "seq_tokens_per_s", "kernels_ms", "roofline", "prefill_roofline", "cache_write")
     out = {k: r[k] for k in keys if k in r}
     out["step_us"] = round(r["ms_per_step"] * 1e3, 2)
     out["workload"] = r["config"]["workload"]
