@@ -73,6 +73,10 @@ def parse():
                          "pa_copy_blocks on the workload's pool")
     ap.add_argument("--copy-seqs", type=int, default=8,
                     help="sequences whose blocks a copy op moves")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="prefix-sharing workload: pa_decode_shared_prefix (prefix pass, "
+                         "suffix pass, reduce) instead of the plain decode, which is faster "
+                         "on MI355X; both step times are reported")
     ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
                     help="chunked-prefill workloads: 2 runs decode and prefill on two streams "
                          "of equal priority (and also times the serial step)")
@@ -233,10 +237,13 @@ METRICS = {
                              "(% of bf16 MFMA peak)",
 }
 # The other workloads the default run measures after the headline one.
-EXTRA_WORKLOADS = [("tiny_decode", False), ("long_context_decode", False),
-                   ("prefix_sharing_decode", False), ("mixed_chunked_prefill", False),
-                   ("llama8b_decode", True), ("long_context_decode", True),
-                   ("prefix_sharing_decode", True), ("mixed_chunked_prefill", True)]
+# (workload, FP8 pools, shared-prefix call)
+EXTRA_WORKLOADS = [("tiny_decode", False, False), ("long_context_decode", False, False),
+                   ("prefix_sharing_decode", False, False),
+                   ("prefix_sharing_decode", False, True),
+                   ("mixed_chunked_prefill", False, False),
+                   ("llama8b_decode", True, False), ("long_context_decode", True, False),
+                   ("prefix_sharing_decode", True, False), ("mixed_chunked_prefill", True, False)]
 
 
 def main():
@@ -265,18 +272,20 @@ def main():
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, dev)
     result, reps = measure(case, dev, fp8, args.partition_size, args.steps, args.warmup,
-                           args.replicas, args.streams)
+                           args.replicas, args.streams, args.shared_prefix)
     del reps
     torch.cuda.empty_cache()
     ceilings = None
     if full_run and not args.no_extra:
         result["workloads"] = {}
-        for wname, wfp8 in EXTRA_WORKLOADS:
+        for wname, wfp8, wsp in EXTRA_WORKLOADS:
             wcase = case if wname == name else W.NAMED[wname]()
-            r, wreps = measure(wcase, dev, wfp8, 0, args.steps, args.warmup, args.replicas)
+            r, wreps = measure(wcase, dev, wfp8, 0, args.steps, args.warmup, args.replicas,
+                               shared_prefix=wsp)
             del wreps
             torch.cuda.empty_cache()
-            result["workloads"][wname + ("_fp8" if wfp8 else "")] = summary(r)
+            key = wname + ("_fp8" if wfp8 else "") + ("_shared_prefix_call" if wsp else "")
+            result["workloads"][key] = summary(r)
         ceilings = measure_ceilings(dev, result["roofline"]["algorithmic_bytes_per_launch"])
         result["ceilings"] = ceilings
         attach_attainable(result, ceilings)
@@ -300,7 +309,7 @@ def copy_probe(mib, dev):
     print(f"copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
-def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
+def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix=False):
     """Times `steps` steps of the hot path on one workload (after `warmup`
     untimed ones), then the same steps again with an event around each kernel
     for the per-kernel breakdown.  Returns (result dict, device replicas)."""
@@ -314,6 +323,11 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
     reps = [Replica(case, dev, fp8) for _ in range(max(1, replicas))]
     ws = binding.make_workspace(reps[0].q, reps[0].kc, maxL, P)
     stream = torch.cuda.current_stream()
+    # The prefix-sharing batch (bf16): pa_decode_shared_prefix, which reads the
+    # shared blocks once per tile of sequences instead of once per sequence.
+    pb = case.shared_blocks.numel() if case.shared_blocks is not None else 0
+    sp = bool(shared_prefix and pb and not fp8 and case.dtype == "bf16" and P == 0)
+    ws_sp = binding.make_shared_prefix_workspace(reps[0].q, reps[0].kc, maxL, pb) if sp else None
 
     # Algorithmic work per step.
     unique = None
@@ -355,6 +369,13 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
             binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
         if record:
             ev["dp0"].append(mark("cw1"))
+        if sp:  # prefix pass, suffix pass and reduce in one call
+            binding.decode_shared_prefix(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL,
+                                         pb, workspace=ws_sp, stream=stream)
+            if record:
+                mark("dp1")
+                mark("dr1")
+            return
         if fp8 and fused:
             binding.decode_fp8_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
                                                  r.lens, case.scale, maxL, FP8_K_SCALE,
@@ -451,6 +472,13 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
     print(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
     serial_ms = timed(lambda i: step(i, False), steps)[0] if overlap else None
+    plain_ms = None
+    if sp:  # the same batch through the plain balanced decode, for comparison
+        sp = False
+        for i in range(warmup):
+            step(i, False)
+        plain_ms = timed(lambda i: step(i, False), steps)[0]
+        sp = True
     for i in range(steps):
         step(i, True)
     torch.cuda.synchronize()
@@ -468,7 +496,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
 
     t_cw = avg_ms("cw0", "cw1") if T and not fused else None
     t_dp = avg_ms("dp0", "dp1")
-    t_dr = avg_ms("dp1", "dr1")
+    t_dr = avg_ms("dp1", "dr1") if not sp else None  # inside the one call
     t_pf = avg_ms("pf0", "pf1") if chunks else None
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
@@ -479,6 +507,8 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
                  "decode_stream_mma_kernel" if case.dtype == "bf16" else "decode_stream_kernel")
     # The fused step's decode kernel also moves the new tokens' rows.
     dp_bytes = dec_bytes + (cw_bytes if fused else 0)
+    if sp:  # one call: prefix pass + suffix pass + reduce
+        dp_kernel = "pa_decode_shared_prefix"
     result = {
         "metric": METRICS[case.name] + (", FP8 e4m3 KV cache" if fp8 else ""),
         "value": round(value, 2),
@@ -497,6 +527,8 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
+            "decode": ("pa_decode_shared_prefix (prefix pass, suffix pass, reduce)" if sp
+                       else "pa_decode_partitions + pa_decode_reduce"),
             "cache_write": ("fused into the decode pass (pa_decode_fp8_append)" if fused and fp8
                             else "fused into the decode pass (pa_decode_append)" if fused
                             else "pa_reshape_and_cache_fp8" if T and fp8
@@ -510,8 +542,10 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1):
         "seq_tokens_per_s": round(sum(lens) / (ms_step * 1e-3), 1),
         "new_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "serial_ms_per_step": _r(serial_ms),
+        "plain_decode_ms_per_step": _r(plain_ms),
         "kernels_ms": {"reshape_and_cache": "fused" if fused else _r(t_cw),
-                       "decode_partition": _r(t_dp), "decode_reduce": _r(t_dr),
+                       ("decode_shared_prefix" if sp else "decode_partition"): _r(t_dp),
+                       "decode_reduce": _r(t_dr),
                        "prefill_chunk": _r(t_pf)},
         "roofline": roofline(dp_kernel, wl, "hbm", dp_bytes, t_dp, HBM_PEAK_GBS,
                              medians["dp0dp1"]),
@@ -561,7 +595,8 @@ def roofline(kernel, workload, bound, work, ms, peak, median_ms):
 
 def summary(r):
     """The per-workload entry of the default run's line."""
-    keys = ("metric", "value", "unit", "ms_per_step", "serial_ms_per_step", "hbm_frac",
+    keys = ("metric", "value", "unit", "ms_per_step", "serial_ms_per_step",
+            "plain_decode_ms_per_step", "hbm_frac",
             "seq_tokens_per_s", "kernels_ms", "roofline", "prefill_roofline", "cache_write")
     out = {k: r[k] for k in keys if k in r}
     out["step_us"] = round(r["ms_per_step"] * 1e3, 2)

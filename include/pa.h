@@ -193,6 +193,46 @@ pa_status pa_decode_no_alloc(void *out, const void *query, const void *key_cache
 size_t pa_decode_no_alloc_max_workspace(void);
 
 /*
+ * pa_decode_shared_prefix -- decode (bf16) for a batch whose sequences all
+ * start with the same prompt blocks: entries 0 .. prefix_blocks - 1 of every
+ * row of block_tables name the same physical blocks (a common prompt reused
+ * through prefix caching: "Configuring vLLM and PagedAttention for High
+ * Throughput Enterprise LLM Serving", section "Zero-Copy Prefix Caching &
+ * Shared Sampling"; "vLLM High-Performance Inference Engine: PagedAttention
+ * Principles and Deployment Guide", section "PagedAttention Architecture Deep
+ * Dive").  The result is that of pa_decode on the same arguments (dtype
+ * bf16), up to fp32 rounding order; pa_decode itself stays unchanged.
+ *
+ * Instead of streaming the prefix blocks once per sequence, one pass attends
+ * the queries of all sequences to them (16 / G sequences per matrix-core
+ * tile, so each K/V byte of the prefix is read once per tile), a second pass
+ * streams each sequence's tokens past the prefix (the balanced split of
+ * pa_decode), and the reduce merges both sets of partial results with
+ * log-sum-exp rescaling.  A sequence with context_lens[s] <= prefix_blocks *
+ * block_size attends to its own first context_lens[s] tokens only.
+ *
+ * Arguments as pa_decode, plus prefix_blocks in [0, max_blocks_per_seq]
+ * (0: the plain balanced decode); num_seqs at most 8192 (else
+ * PA_ERR_UNSUPPORTED); workspace (256-byte aligned) of at least
+ * pa_decode_shared_prefix_workspace_bytes() bytes, else PA_ERR_WORKSPACE.
+ * Equal prefix rows are the caller's contract; with PA_DEBUG=1 they are
+ * checked on the host (PA_ERR_INVALID_ARG).
+ */
+pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t max_context_len,
+                                  int32_t prefix_blocks, float scale, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t max_context_len,
+                                               int32_t prefix_blocks);
+
+/*
  * The two phases of pa_decode, callable on their own (same arguments; the
  * pair enqueued back to back on one stream is exactly pa_decode).
  * pa_decode_partitions writes the final output of every sequence that fits in

@@ -50,6 +50,9 @@ SIGNATURES = {
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
+    "pa_decode_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _i32, _i64, _i32, _i32, _f, _vp, _sz, _vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_probe_sink_words": (_i64, []),
     "pa_probe_stream_read": (_i32, [_vp, _i64, _vp, _vp]),
     "pa_probe_mfma_bf16": (_i32, [_vp, _i32, ctypes.POINTER(ctypes.c_double), _vp]),
@@ -206,6 +209,36 @@ def decode_no_alloc(out, query, key_cache, value_cache, block_tables, context_le
     args = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                         max_context_len, partition_size, scale, None)[:-2]
     _check(load().pa_decode_no_alloc(*args, _stream(stream)))
+    return out
+
+
+def shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  max_context_len, prefix_blocks) -> int:
+    return int(load().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        prefix_blocks))
+
+
+def make_shared_prefix_workspace(query, key_cache, max_context_len, prefix_blocks):
+    S, Hq, D = query.shape
+    _, Hkv, B, _ = key_cache.shape
+    n = shared_prefix_workspace_bytes(S, Hq, Hkv, D, B, max_context_len, prefix_blocks)
+    return torch.empty(n, dtype=torch.uint8, device=query.device)
+
+
+def decode_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens, scale,
+                         max_context_len, prefix_blocks, workspace=None, stream=None):
+    """Decode (bf16) for a batch whose block-table rows all start with the
+    same prefix_blocks physical blocks; writes ``out`` [S, Hq, D]."""
+    if workspace is None:
+        workspace = make_shared_prefix_workspace(query, key_cache, max_context_len,
+                                                 prefix_blocks)
+    a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                     max_context_len, 0, scale, workspace)
+    if a[16] != PA_BF16:
+        raise PAError(PA_ERR_UNSUPPORTED, "the shared-prefix decode is bf16 only")
+    _check(load().pa_decode_shared_prefix(*a[:14], int(prefix_blocks), a[15], a[17], a[18],
+                                          _stream(stream)))
     return out
 
 

@@ -48,6 +48,7 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_prefix.h"
 
 namespace pa {
 
@@ -338,22 +339,27 @@ __device__ __forceinline__ int clamp_len(int L, int max_tokens) {
     return L < 0 ? 0 : (L > max_tokens ? max_tokens : L);
 }
 
+// Tokens of a length-L sequence past its first skip (none when L <= skip).
+__device__ __forceinline__ int past_skip(int L, int skip) { return L > skip ? L - skip : 0; }
+
 // Wave (of nw <= U) whose range [U*w/nw, U*(w+1)/nw) contains unit u < U.
 __device__ __forceinline__ int wave_of_unit(int64_t u, int64_t U, int nw) {
     return (int)(((u + 1) * nw - 1) / U);
 }
 
 // Exclusive scan of the per-sequence unit counts into scan[0..S], by a
-// workgroup of NW waves.  scan[S] is the total per kv head.
+// workgroup of NW waves.  scan[S] is the total per kv head.  Sequence s counts
+// context_lens[s] - len_skip tokens (its tokens past the first len_skip).
 template <int NW>
 __device__ void scan_units(int *scan, const int32_t *__restrict__ context_lens, int S,
-                           int max_tokens) {
+                           int max_tokens, int len_skip = 0) {
     __shared__ int wave_sums[NW];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int per = cdiv(S, NW * 64);
     const int lo = min(S, t * per), hi = min(S, lo + per);
     int sum = 0;
-    for (int s = lo; s < hi; ++s) sum += cdiv(clamp_len(context_lens[s], max_tokens), kUnitTokens);
+    for (int s = lo; s < hi; ++s)
+        sum += cdiv(clamp_len(past_skip(context_lens[s], len_skip), max_tokens), kUnitTokens);
     int incl = sum;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -370,7 +376,7 @@ __device__ void scan_units(int *scan, const int32_t *__restrict__ context_lens, 
     }
     for (int s = lo; s < hi; ++s) {
         scan[s] = run;
-        run += cdiv(clamp_len(context_lens[s], max_tokens), kUnitTokens);
+        run += cdiv(clamp_len(past_skip(context_lens[s], len_skip), max_tokens), kUnitTokens);
     }
     if (t == 0) scan[S] = total;
     __syncthreads();
@@ -682,7 +688,8 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
     const int32_t *__restrict__ context_lens, int S, int num_q_heads, int num_kv_heads,
     int max_blocks, int max_tokens, int64_t num_blocks, int nw, float scale_log2,
     float *__restrict__ rec_o, float *__restrict__ rec_ml, int *__restrict__ ws_scan,
-    const bf16_t *__restrict__ new_key, const bf16_t *__restrict__ new_value) {
+    const bf16_t *__restrict__ new_key, const bf16_t *__restrict__ new_value, int len_skip,
+    int force_records) {
     constexpr int ROWB = D * 2, NCH = ROWB / 16, KS = D / 32, DT = D / 16;
     constexpr int UNIT_BYTES = kUnitTokens * ROWB, NB = kMmaBuffers;
     constexpr int KPS = 1024 / ROWB;               // rows per 1 KB DMA segment
@@ -690,7 +697,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
     static_assert(G <= 16, "group fits the 16 columns");
     extern __shared__ int scan[];                  // [S + 1], sized at launch
     __shared__ __attribute__((aligned(1024))) char vslot[NW][NB][UNIT_BYTES];
-    scan_units<NW>(scan, context_lens, S, max_tokens);
+    scan_units<NW>(scan, context_lens, S, max_tokens, len_skip);
     const int Hkv = num_kv_heads;
     const int64_t U = (int64_t)scan[S] * Hkv;
     if (blockIdx.x == 0)
@@ -747,7 +754,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
     auto finish = [&]() __attribute__((always_inline)) {
         const int us = scan[cur_s + 1] - scan[cur_s];
         const int64_t u0 = (int64_t)scan[cur_s] * Hkv + (int64_t)cur_g * us;
-        const bool whole = u0 >= ua && u0 + us <= ub;
+        const bool whole = !force_records && u0 >= ua && u0 + us <= ub;
         const float lsum = __shfl(acc_l[0], l16);
         if (l16 >= G) return;
         const int64_t qrow = (int64_t)cur_s * num_q_heads + (int64_t)cur_g * G + l16;
@@ -808,7 +815,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
                                              (int64_t)it * ROWB + c2ch * 16);
         }
         if (lane < n) {
-            const int Lraw = context_lens[l_s];
+            const int Lraw = past_skip(context_lens[l_s], len_skip);
             const int L = clamp_len(Lraw, max_tokens);
             const int tok = l_j * kUnitTokens;
             l_nvalid = min(kUnitTokens, L - tok);
@@ -952,6 +959,193 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
         }
     }
     if (cur_item >= 0) finish();
+}
+
+// ---------------------------------------------------------------------------
+// Shared prefix (bf16).  When the first P tokens of every sequence lie in the
+// same physical blocks (a common prompt reused through prefix caching:
+// "Configuring vLLM and PagedAttention for High Throughput Enterprise LLM
+// Serving", section "Zero-Copy Prefix Caching & Shared Sampling"), the decode
+// kernels above stream those blocks once per sequence.  This kernel reads them
+// once per group of sequences: the 16 MFMA columns of a wave carry 16 / G
+// sequences x the G query heads of one kv head, so every K/V unit it loads
+// serves all of them.  A wave covers a 1 / ksplit share of the prefix's units
+// and writes one record (m, l, unnormalised o) per column; the reduce merges
+// those with the records of the balanced split over each sequence's tokens
+// past P.  Column c's keys stop at min(L_s, P), so a sequence no longer than
+// the prefix attends to its own tokens only.  Products, softmax and V path are
+// those of decode_stream_mma_kernel.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+template <int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_prefix_mma_kernel(
+    const bf16_t *__restrict__ query, const bf16_t *__restrict__ key_cache,
+    const bf16_t *__restrict__ value_cache, const int32_t *__restrict__ prefix_table,
+    const int32_t *__restrict__ context_lens, int S, int num_q_heads, int num_kv_heads,
+    int64_t num_blocks, int prefix_tokens, int ksplit, float scale_log2, float *__restrict__ x_o,
+    float *__restrict__ x_ml) {
+    constexpr int ROWB = D * 2, NCH = ROWB / 16, KS = D / 32, DT = D / 16;
+    constexpr int UNIT_BYTES = kUnitTokens * ROWB, NB = kMmaBuffers;
+    constexpr int KPS = 1024 / ROWB;               // rows per 1 KB DMA segment
+    constexpr int SEGS = UNIT_BYTES / 1024;        // DMA instructions per unit
+    constexpr int CPW = 16 / G;                    // sequences per wave
+    __shared__ __attribute__((aligned(1024))) char vslot[NW][NB][UNIT_BYTES];
+
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int Hkv = num_kv_heads;
+    const int ncg = cdiv(S, CPW);
+    // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+    // L2).  Renumber them so that consecutive wave numbers, which share a kv
+    // head and so read the same prefix pages, run on one XCD.
+    const int total = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid % kXcds, idx = bid / kXcds;
+    const int q8 = total / kXcds, rem = total % kXcds;
+    const int lin = xcd < rem ? xcd * (q8 + 1) + idx : rem * (q8 + 1) + (xcd - rem) * q8 + idx;
+    const int gw = lin * NW + w;
+    const int k = gw % ksplit, rest = gw / ksplit;
+    const int cg = rest % ncg, g = rest / ncg;
+    if (g >= Hkv) return;
+
+    // This lane's column: sequence s, head hh of kv head g.
+    const int s = cg * CPW + l16 / G, hh = l16 % G;
+    const bool col_ok = s < S;
+    int lim = 0;
+    if (col_ok) {
+        const int L = context_lens[s];
+        lim = L < 0 ? 0 : min(L, prefix_tokens);
+    }
+    const int nu = cdiv(prefix_tokens, kUnitTokens);
+    const int u0 = (int)((int64_t)nu * k / ksplit), u1 = (int)((int64_t)nu * (k + 1) / ksplit);
+
+    const int64_t head_bytes = (int64_t)B * ROWB;
+    const int64_t block_bytes = head_bytes * Hkv;
+    const char *kbase = (const char *)key_cache;
+    const char *vbase = (const char *)value_cache;
+    const int k_off = l16 * ROWB + lg * 16;
+    const int dma_row = lane / NCH, dma_ch = lane % NCH;
+    const int v_row = 4 * lg + (l16 >> 2);
+    const uint32_t v_lane =
+        v_row * ROWB + (l16 & 1) * 8 + ((mma_swz<D>(v_row) ^ ((l16 & 3) >> 1)) << 4);
+    const s16x4_mv ones_a = l16 == 0 ? s16x4_mv{0x3F80, 0x3F80, 0x3F80, 0x3F80} : s16x4_mv{0, 0, 0, 0};
+
+    u32x4 qt[KS];
+    {
+        const char *qrow = (const char *)query +
+                           ((int64_t)(col_ok ? s : 0) * num_q_heads + (int64_t)g * G + hh) * ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = *(const u32x4 *)(qrow + ks * 64 + lg * 16);
+            qt[ks] = col_ok ? v : u32x4{0, 0, 0, 0};
+        }
+    }
+    f32x4_mv acc_o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x4_mv{0.f, 0.f, 0.f, 0.f};
+    f32x4_mv acc_l = {0.f, 0.f, 0.f, 0.f};
+    float m_col = NEG_INF;
+
+    for (int c0 = u0; c0 < u1; c0 += 64) {
+        const int n = min(64, u1 - c0);
+        // Lane j: unit c0 + j of the prefix (its page from row 0 of the table).
+        int l_nvalid = 0, l_phys = 0, l_tokoff = 0;
+        if (lane < n) {
+            const int tok = (c0 + lane) * kUnitTokens;
+            l_nvalid = min(kUnitTokens, prefix_tokens - tok);
+            l_tokoff = tok % B;
+            const int phys = prefix_table[tok / B];
+            if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
+            l_phys = phys;
+        }
+
+        u32x4 kb[NB][KS];
+        int nv[NB], ut[NB];
+        auto issue = [&](int b, int i) __attribute__((always_inline)) {
+            const int ii = i & 63;
+            const int nvalid = i < n ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
+            const int phys = __builtin_amdgcn_readlane(l_phys, ii);
+            const int tokoff = __builtin_amdgcn_readlane(l_tokoff, ii);
+            const int64_t off = nvalid > 0 ? (int64_t)phys * block_bytes + (int64_t)g * head_bytes +
+                                                 (int64_t)tokoff * ROWB
+                                           : 0;
+            const int range = nvalid > 0 ? nvalid * ROWB : 0;
+            nv[b] = nvalid;
+            ut[b] = (c0 + i) * kUnitTokens;
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + off), (short)0, range, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + off), (short)0, range, 0x00020000);
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const int row = sg * KPS + dma_row;
+                dma16_to_lds(rv, &vslot[w][b][sg * 1024],
+                             row * ROWB + ((dma_ch ^ mma_swz<D>(row)) << 4));
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kb[b][ks] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + ks * 64, 0, 0));
+        };
+
+        auto process = [&](int b) __attribute__((always_inline)) {
+            f32x4_mv st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_mv, kb[b][ks]),
+                                                             __builtin_bit_cast(bf16x8_mv, qt[ks]),
+                                                             st, 0, 0, 0);
+            const uint32_t vb = lds_offset(&vslot[w][b][0]) + v_lane;
+            s16x4_mv va[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_tr16(vb ^ ((uint32_t)dt << 5));
+            float x[4];
+            bool need = m_col == NEG_INF;
+            float lmax = NEG_INF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (ut[b] + 4 * lg + i < lim) ? st[i] * scale_log2 : NEG_INF;
+                lmax = fmaxf(lmax, x[i]);
+            }
+            need |= lmax > m_col + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = fmaxf(m_col, max4_lanes(lmax));
+                const float alpha = (m_col == NEG_INF) ? 0.f : fast_exp2(m_col - mn);
+                m_col = mn;
+                acc_l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+            }
+            const float mneg = (m_col == NEG_INF) ? 0.f : -m_col;
+            uint32_t p01 = pack_bf16x2(fast_exp2(x[0] + mneg), fast_exp2(x[1] + mneg));
+            uint32_t p23 = pack_bf16x2(fast_exp2(x[2] + mneg), fast_exp2(x[3] + mneg));
+            const s16x4_mv pt = __builtin_bit_cast(s16x4_mv, (uint64_t)p01 | ((uint64_t)p23 << 32));
+            acc_l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones_a, pt, acc_l, 0, 0, 0);
+            if constexpr (DT == 8) lds_tr_wait<8>(va); else lds_tr_wait<4>(va);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pt, acc_o[dt], 0, 0, 0);
+        };
+
+#pragma unroll
+        for (int b = 0; b < NB; ++b) issue(b, b);
+        for (int i = 0; i < n; i += NB) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (nv[b] > 0) process(b);
+                issue(b, i + NB + b);
+            }
+        }
+    }
+
+    const float lsum = __shfl(acc_l[0], l16);
+    if (!col_ok) return;
+    const int64_t rid = ((int64_t)s * num_q_heads + (int64_t)g * G + hh) * ksplit + k;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        *(float4 *)(x_o + rid * D + dt * 16 + lg * 4) =
+            make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    if (lg == 0) *(float2 *)(x_ml + rid * 2) = make_float2(m_col, lsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -1323,21 +1517,34 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
 // split softmax results).  Record k's (m, l) pair is at ml + k * ml_stride, its
 // output at o + k * o_stride.  Lane k loads the weights of record k, and the
 // outputs of 8 records are loaded before any is used, so a row costs a few
-// memory round trips rather than one per record.
+// memory round trips rather than one per record.  x_n <= 8 further records
+// (x_ml + 2k, x_o + k * D; the shared-prefix records) join the merge; nrec
+// may then be 0.
 template <typename T, int D>
 __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *__restrict__ ml,
                                               int64_t ml_stride, const float *__restrict__ o,
-                                              int64_t o_stride, int nrec, int lane) {
+                                              int64_t o_stride, int nrec, int lane,
+                                              const float *__restrict__ x_ml = nullptr,
+                                              const float *__restrict__ x_o = nullptr,
+                                              int x_n = 0) {
     constexpr int DPL = D / 64;  // dims per lane
     typedef float vecd __attribute__((ext_vector_type(DPL)));
     float2 w0 = make_float2(NEG_INF, 0.f);
     if (lane < nrec) w0 = *(const float2 *)(ml + lane * ml_stride);
+    float2 xw = make_float2(NEG_INF, 0.f);
+    if (lane < x_n) xw = *(const float2 *)(x_ml + 2 * lane);
     // The outputs of the first 8 records go out with the weights (they do not
     // depend on them), so a row of up to 8 records costs one round trip.
-    vecd v0[8];
+    vecd v0[8], xv[8];
+    if (nrec > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v0[j] = *(const vecd *)(o + min(j, nrec - 1) * o_stride + lane * DPL);
-    float M = w0.x;
+        for (int j = 0; j < 8; ++j)
+            v0[j] = *(const vecd *)(o + min(j, nrec - 1) * o_stride + lane * DPL);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < x_n) xv[j] = *(const vecd *)(x_o + (int64_t)j * D + lane * DPL);
+    float M = fmaxf(w0.x, xw.x);
     for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, ml[k * ml_stride]);
     M = wave_max(M);
     float lsum = 0.f;
@@ -1365,6 +1572,14 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
             }
         }
     }
+    if (x_n > 0) {
+        const float fx = (xw.x == NEG_INF) ? 0.f : fast_exp2(xw.x - M);  // 0 past x_n
+        lsum = fmaf(fx, xw.y, lsum);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < x_n)
+                acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fx), j)) * xv[j];
+    }
     lsum = group_sum<16>(lsum);
     lsum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 0)) +
            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 16)) +
@@ -1378,10 +1593,13 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
 // Merge the partial records of each (sequence, q head): records of pair i
 // come from waves wave_of_unit(first unit) .. wave_of_unit(last unit), stored
 // at record i + wave.  One wave per output row.
+// x_n > 0: every row also merges its x_n shared-prefix records (x_o [row][x_n][D],
+// x_ml [row][x_n][2]), and the decode kernel wrote every pair as records.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     T *__restrict__ out, const int *__restrict__ ws_scan, int S, int num_q_heads,
-    int num_kv_heads, int nw, const float *__restrict__ rec_o, const float *__restrict__ rec_ml) {
+    int num_kv_heads, int nw, const float *__restrict__ rec_o, const float *__restrict__ rec_ml,
+    const float *__restrict__ x_o, const float *__restrict__ x_ml, int x_n) {
     constexpr int DPL = D / 64;  // dims per lane
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1390,7 +1608,13 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     const int G = num_q_heads / num_kv_heads;
     const int g = h / G, hh = h - g * G;
     const int us = ws_scan[s + 1] - ws_scan[s];
+    const float *xo = x_n > 0 ? x_o + row * x_n * D : nullptr;
+    const float *xml = x_n > 0 ? x_ml + row * x_n * 2 : nullptr;
     if (us == 0) {
+        if (x_n > 0) {
+            merge_records<T, D>(out + row * D, nullptr, 0, nullptr, 0, 0, lane, xml, xo, x_n);
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < DPL; ++e) Elem<T>::store(out + row * D + lane * DPL + e, 0.f);
         return;
@@ -1399,11 +1623,11 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     const int nwe = (int)min((int64_t)nw, U);  // the waves that worked (us > 0, so U > 0)
     const int64_t u0 = (int64_t)ws_scan[s] * num_kv_heads + (int64_t)g * us;
     const int w0 = wave_of_unit(u0, U, nwe), w1 = wave_of_unit(u0 + us - 1, U, nwe);
-    if (w0 == w1) return;  // finished by its wave
+    if (w0 == w1 && x_n == 0) return;  // finished by its wave
     const int64_t item = (int64_t)s * num_kv_heads + g;
     const int64_t rid0 = (item + w0) * G + hh;
     merge_records<T, D>(out + row * D, rec_ml + rid0 * 2, 2 * G, rec_o + rid0 * D, (int64_t)G * D,
-                        w1 - w0 + 1, lane);
+                        w1 - w0 + 1, lane, xml, xo, x_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -1570,7 +1794,8 @@ static int max_tokens(const DecodeArgs &a) {
 #endif
 
 template <int D, int B, int G>
-static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream) {
+static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream, int len_skip = 0,
+                                    int force_records = 0) {
     const dim3 grid(cdiv(a.stream_waves, kMmaWaves));
     const size_t dyn = (size_t)(a.num_seqs + 1) * sizeof(int);
     if (a.new_key)
@@ -1580,7 +1805,8 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream) {
                            a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads,
                            a.num_kv_heads, a.max_blocks_per_seq, max_tokens(a), a.num_blocks,
                            a.stream_waves, a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
-                           (const bf16_t *)a.new_key, (const bf16_t *)a.new_value);
+                           (const bf16_t *)a.new_key, (const bf16_t *)a.new_value, len_skip,
+                           force_records);
     else
         hipLaunchKernelGGL((decode_stream_mma_kernel<D, B, G, kMmaWaves, false>), grid,
                            dim3(kMmaWaves * 64), dyn, stream, (bf16_t *)a.out,
@@ -1588,7 +1814,8 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream) {
                            a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads,
                            a.num_kv_heads, a.max_blocks_per_seq, max_tokens(a), a.num_blocks,
                            a.stream_waves, a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
-                           (const bf16_t *)nullptr, (const bf16_t *)nullptr);
+                           (const bf16_t *)nullptr, (const bf16_t *)nullptr, len_skip,
+                           force_records);
     return hipGetLastError();
 }
 
@@ -1702,12 +1929,14 @@ hipError_t launch_decode_partitions(const DecodeArgs &a, hipStream_t stream) {
 }
 
 template <typename T, int D>
-static hipError_t launch_red(const DecodeArgs &a, hipStream_t stream) {
+static hipError_t launch_red(const DecodeArgs &a, hipStream_t stream,
+                             const PrefixArgs *px = nullptr) {
     const unsigned blocks = (unsigned)cdiv((int)((int64_t)a.num_seqs * a.num_q_heads), 4);
     if (a.stream_waves > 0) {
         hipLaunchKernelGGL((decode_stream_reduce_kernel<T, D>), dim3(blocks), dim3(256), 0,
                            stream, (T *)a.out, a.ws_scan, a.num_seqs, a.num_q_heads,
-                           a.num_kv_heads, a.stream_waves, a.ws_o, a.ws_ml);
+                           a.num_kv_heads, a.stream_waves, a.ws_o, a.ws_ml,
+                           px ? px->x_o : nullptr, px ? px->x_ml : nullptr, px ? px->ksplit : 0);
     } else {
         hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(blocks), dim3(256), 0, stream,
                            (T *)a.out, a.context_lens, a.num_seqs, a.num_q_heads, max_tokens(a),
@@ -1722,6 +1951,88 @@ hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream) {
         return a.head_dim == 64 ? launch_red<bf16_t, 64>(a, stream)
                                 : launch_red<bf16_t, 128>(a, stream);
     return a.head_dim == 64 ? launch_red<float, 64>(a, stream) : launch_red<float, 128>(a, stream);
+}
+
+
+// ---- shared prefix --------------------------------------------------------
+
+// Waves the prefix pass aims for: the splits of the prefix grow until the
+// (kv head, column group) pairs times the splits reach one wave per SIMD.
+// (Two or eight splits on the 128-sequence, 1,024-token prefix took longer.)
+constexpr int kPrefixWaves = 1024;
+
+static int64_t cdiv_i64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int prefix_splits(int num_seqs, int num_q_heads, int num_kv_heads, int prefix_tokens) {
+    const int G = num_q_heads / num_kv_heads;
+    const int64_t ncg = cdiv(num_seqs, 16 / G);
+    const int64_t units = cdiv(prefix_tokens, kUnitTokens);
+    int64_t k = cdiv_i64(kPrefixWaves, (int64_t)num_kv_heads * ncg);
+    if (k > kPrefixMaxSplits) k = kPrefixMaxSplits;
+    if (k > units) k = units;
+    return k < 1 ? 1 : (int)k;
+}
+
+template <int D, int B, int G>
+static hipError_t launch_prefix_as(const DecodeArgs &a, const PrefixArgs &p, hipStream_t stream) {
+    const int64_t waves = (int64_t)a.num_kv_heads * cdiv(a.num_seqs, 16 / G) * p.ksplit;
+    hipLaunchKernelGGL((decode_prefix_mma_kernel<D, B, G, kMmaWaves>),
+                       dim3((unsigned)cdiv_i64(waves, kMmaWaves)), dim3(kMmaWaves * 64), 0, stream,
+                       (const bf16_t *)a.query, (const bf16_t *)a.key_cache,
+                       (const bf16_t *)a.value_cache, p.prefix_table, a.context_lens, a.num_seqs,
+                       a.num_q_heads, a.num_kv_heads, a.num_blocks, p.prefix_tokens, p.ksplit,
+                       a.scale * kLog2e, p.x_o, p.x_ml);
+    return hipGetLastError();
+}
+
+template <int D, int B>
+static hipError_t prefix_by_group(const DecodeArgs &a, const PrefixArgs &p, hipStream_t stream) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_prefix_as<D, B, 1>(a, p, stream);
+        case 2: return launch_prefix_as<D, B, 2>(a, p, stream);
+        case 4: return launch_prefix_as<D, B, 4>(a, p, stream);
+        case 8: return launch_prefix_as<D, B, 8>(a, p, stream);
+    }
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_decode_prefix(const DecodeArgs &a, const PrefixArgs &p, hipStream_t stream) {
+    if (a.num_seqs == 0 || p.prefix_tokens == 0) return hipSuccess;
+    if (a.dtype != 1 || a.kv_fp8) return hipErrorNotSupported;
+    if (a.head_dim == 64)
+        return a.block_size == 16 ? prefix_by_group<64, 16>(a, p, stream)
+                                  : prefix_by_group<64, 32>(a, p, stream);
+    return a.block_size == 16 ? prefix_by_group<128, 16>(a, p, stream)
+                              : prefix_by_group<128, 32>(a, p, stream);
+}
+
+template <int D, int B>
+static hipError_t suffix_by_group(const DecodeArgs &a, int len_skip, hipStream_t stream) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_stream_mma<D, B, 1>(a, stream, len_skip, 1);
+        case 2: return launch_stream_mma<D, B, 2>(a, stream, len_skip, 1);
+        case 4: return launch_stream_mma<D, B, 4>(a, stream, len_skip, 1);
+        case 8: return launch_stream_mma<D, B, 8>(a, stream, len_skip, 1);
+    }
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_decode_suffix(const DecodeArgs &a, int len_skip, hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    if (a.dtype != 1 || a.kv_fp8 || a.stream_waves == 0 || a.new_key) return hipErrorNotSupported;
+    if (a.head_dim == 64)
+        return a.block_size == 16 ? suffix_by_group<64, 16>(a, len_skip, stream)
+                                  : suffix_by_group<64, 32>(a, len_skip, stream);
+    return a.block_size == 16 ? suffix_by_group<128, 16>(a, len_skip, stream)
+                              : suffix_by_group<128, 32>(a, len_skip, stream);
+}
+
+hipError_t launch_decode_reduce_prefix(const DecodeArgs &a, const PrefixArgs &p,
+                                       hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    if (a.dtype != 1 || a.stream_waves == 0) return hipErrorNotSupported;
+    return a.head_dim == 64 ? launch_red<bf16_t, 64>(a, stream, &p)
+                            : launch_red<bf16_t, 128>(a, stream, &p);
 }
 
 }  // namespace pa

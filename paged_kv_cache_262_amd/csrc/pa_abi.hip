@@ -12,6 +12,7 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_prefix.h"
 #include "pa_probes.h"
 
 namespace {
@@ -266,6 +267,38 @@ pa_status debug_decode(const pa::DecodeArgs &a, hipStream_t stream) {
     if (s != PA_OK) return s;
     return check_table_rows(bt, lens, a.max_blocks_per_seq, a.block_size, a.num_blocks,
                             "block_tables");
+}
+
+// Shared-prefix decode: the full-table checks of debug_decode, and the first
+// prefix_blocks entries of every row equal to those of row 0.
+pa_status debug_shared_prefix(const int32_t *block_tables, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t max_blocks, int32_t block_size,
+                              int64_t num_blocks, int32_t max_context_len, int32_t prefix_blocks,
+                              hipStream_t stream) {
+    if (num_seqs <= 0) return PA_OK;
+    std::vector<int32_t> lens, bt;
+    pa_status s = fetch(lens, context_lens, (size_t)num_seqs, stream, "context_lens");
+    if (s != PA_OK) return s;
+    for (int32_t i = 0; i < num_seqs; ++i)
+        if (lens[i] < 0 || lens[i] > max_context_len)
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: context_lens[%d] = %d outside [0, %d]", i,
+                        lens[i], max_context_len);
+    s = fetch(bt, block_tables, (size_t)num_seqs * max_blocks, stream, "block_tables");
+    if (s != PA_OK) return s;
+    s = check_table_rows(bt, lens, max_blocks, block_size, num_blocks, "block_tables");
+    if (s != PA_OK) return s;
+    for (int32_t j = 0; j < prefix_blocks; ++j)
+        if (bt[j] < 0 || (int64_t)bt[j] >= num_blocks)
+            return fail(PA_ERR_INVALID_ARG, "PA_DEBUG: prefix block %d = %d outside the pool", j,
+                        bt[j]);
+    for (int32_t i = 1; i < num_seqs; ++i)
+        for (int32_t j = 0; j < prefix_blocks; ++j)
+            if (bt[(size_t)i * max_blocks + j] != bt[j])
+                return fail(PA_ERR_INVALID_ARG,
+                            "PA_DEBUG: block_tables[%d][%d] = %d differs from the shared prefix "
+                            "block %d",
+                            i, j, bt[(size_t)i * max_blocks + j], bt[j]);
+    return PA_OK;
 }
 
 pa_status debug_slots(const int64_t *slot_mapping, int32_t num_tokens, int64_t num_slots,
@@ -536,6 +569,123 @@ pa_status pa_decode_no_alloc(void *out, const void *query, const void *key_cache
                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_context_len, partition_size, scale, dtype, ws,
                      kNoAllocScratchBytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared-prefix decode: the balanced split's workspace for the tokens past
+// the prefix, then the prefix records.
+struct PrefixPlan {
+    DecodePlan suffix;
+    int32_t prefix_tokens, suffix_max_len;
+    int ksplit;
+    size_t xo_bytes, xml_bytes;
+    size_t total() const { return suffix.total() + xo_bytes + xml_bytes; }
+};
+
+PrefixPlan plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                       int32_t prefix_blocks) {
+    PrefixPlan p{};
+    p.prefix_tokens = prefix_blocks * block_size;
+    p.suffix_max_len = max_context_len > p.prefix_tokens ? max_context_len - p.prefix_tokens : 0;
+    p.suffix = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           p.suffix_max_len, 0);
+    p.ksplit = (num_seqs > 0 && p.prefix_tokens > 0)
+                   ? pa::prefix_splits(num_seqs, num_q_heads, num_kv_heads, p.prefix_tokens)
+                   : 0;
+    const size_t recs = (size_t)(num_seqs > 0 ? num_seqs : 0) * num_q_heads * p.ksplit;
+    p.xo_bytes = align256(recs * head_dim * 4);
+    p.xml_bytes = align256(recs * 2 * 4);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t max_context_len,
+                                               int32_t prefix_blocks) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_q_heads % num_kv_heads || prefix_blocks < 0 ||
+        num_seqs > pa::kStreamMaxSeqs)
+        return kMinWorkspace;
+    const PrefixPlan p = plan_prefix(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, prefix_blocks);
+    return p.total() > kMinWorkspace ? p.total() : kMinWorkspace;
+}
+
+pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t max_context_len,
+                                  int32_t prefix_blocks, float scale, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, PA_BF16);
+    if (s != PA_OK) return s;
+    if (num_seqs < 0 || num_seqs > pa::kStreamMaxSeqs)
+        return fail(num_seqs < 0 ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED,
+                    "num_seqs %d outside [0, %d] for the shared-prefix decode", num_seqs,
+                    pa::kStreamMaxSeqs);
+    if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
+    if (prefix_blocks < 0 || prefix_blocks > max_blocks_per_seq)
+        return fail(PA_ERR_INVALID_ARG, "prefix_blocks %d outside [0, %d]", prefix_blocks,
+                    max_blocks_per_seq);
+    if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
+                    (long long)max_blocks_per_seq * block_size);
+    const PrefixPlan plan = plan_prefix(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                        max_context_len, prefix_blocks);
+    if (num_seqs > 0) {
+        if (!workspace)
+            return fail(PA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", plan.total());
+        if (!aligned(workspace, 256))
+            return fail(PA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+        if (workspace_bytes < plan.total())
+            return fail(PA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                        plan.total());
+        CHECK_PTR(block_tables, 4);
+    }
+    // The pass over the tokens past the prefix: the tables advanced past the
+    // prefix pages, lengths and their bound reduced by the prefix.
+    DecodeSetup st;
+    s = setup_decode(st, out, query, key_cache, value_cache,
+                     block_tables ? block_tables + prefix_blocks : nullptr, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                     max_blocks_per_seq, num_blocks, plan.suffix_max_len, 0, scale, PA_BF16,
+                     workspace, workspace_bytes, true);
+    if (s != PA_OK) return s;
+    if (num_seqs == 0) return PA_OK;
+    if (debug_checks() &&
+        (s = debug_shared_prefix(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                 block_size, num_blocks, max_context_len, prefix_blocks,
+                                 (hipStream_t)stream)) != PA_OK)
+        return s;
+    pa::PrefixArgs px;
+    px.prefix_table = block_tables;
+    px.prefix_tokens = plan.prefix_tokens;
+    px.ksplit = plan.ksplit;
+    px.x_o = (float *)((char *)workspace + plan.suffix.total());
+    px.x_ml = (float *)((char *)workspace + plan.suffix.total() + plan.xo_bytes);
+    if (plan.ksplit == 0) {  // no prefix: the plain balanced decode
+        s = hip_status(pa::launch_decode_partitions(st.a, (hipStream_t)stream),
+                       "decode_partitions");
+        if (s != PA_OK) return s;
+        return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
+    }
+    s = hip_status(pa::launch_decode_prefix(st.a, px, (hipStream_t)stream), "decode_prefix");
+    if (s != PA_OK) return s;
+    s = hip_status(pa::launch_decode_suffix(st.a, plan.prefix_tokens, (hipStream_t)stream),
+                   "decode_suffix");
+    if (s != PA_OK) return s;
+    return hip_status(pa::launch_decode_reduce_prefix(st.a, px, (hipStream_t)stream),
+                      "decode_reduce");
 }
 
 pa_status pa_decode_append_partitions(void *out, const void *query, const void *new_key,

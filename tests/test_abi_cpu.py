@@ -213,3 +213,37 @@ def test_probes_reject_bad_arguments_on_the_host(lib):
     assert lib.pa_probe_mfma_bf16(None, 0, None, None) == 1
     assert b"iters" in lib.pa_last_error()
     assert lib.pa_probe_mfma_bf16(None, 5, None, None) == 1
+
+
+def test_shared_prefix_rejects_on_the_host(lib):
+    """Argument checks of pa_decode_shared_prefix that run before any device call."""
+    f = lib.pa_decode_shared_prefix
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int32] * 6 + [ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    args = lambda S=4, mbs=10, maxL=100, pb=2, ws=None, D=128, G=4: (
+        None, None, None, None, None, None, S, 8 * G, 8, D, 16, mbs, 100, maxL, pb, 0.1, ws, 0,
+        None)
+    assert f(*args(pb=-1)) == 1 and b"prefix_blocks" in lib.pa_last_error()
+    assert f(*args(pb=11)) == 1
+    assert f(*args(S=8193)) == 2
+    assert f(*args(maxL=161)) == 1
+    assert f(*args(D=96)) == 2
+    assert f(*args()) == 3 and b"workspace" in lib.pa_last_error()
+    assert f(*args(S=0)) == 0  # nothing to do
+
+
+def test_shared_prefix_workspace_covers_suffix_and_prefix_records(lib):
+    w = lib.pa_decode_shared_prefix_workspace_bytes
+    w.restype = ctypes.c_size_t
+    w.argtypes = [ctypes.c_int32] * 7
+    d = lib.pa_decode_workspace_bytes
+    d.restype = ctypes.c_size_t
+    d.argtypes = [ctypes.c_int32] * 7
+    # no prefix: exactly the balanced decode's workspace
+    assert w(128, 32, 8, 128, 16, 3072, 0) == d(128, 32, 8, 128, 16, 3072, 0)
+    # 128 seqs, 64-block prefix: the suffix split (max 2048 tokens past the
+    # prefix) plus 4 prefix records of 130 floats per (sequence, q head)
+    base = d(128, 32, 8, 128, 16, 3072 - 1024, 0)
+    assert w(128, 32, 8, 128, 16, 3072, 64) == base + 128 * 32 * 4 * 128 * 4 + 128 * 32 * 4 * 8
