@@ -77,6 +77,11 @@ def parse():
                     help="prefix-sharing workload: pa_decode_shared_prefix (prefix pass, "
                          "suffix pass, reduce) instead of the plain decode, which is faster "
                          "on MI355X; both step times are reported")
+    ap.add_argument("--fused-writes", action="store_true",
+                    help="chunked-prefill workloads (bf16): write the new tokens inside the "
+                         "decode pass (pa_decode_append) and the prefill pass "
+                         "(pa_prefill_chunk_append) instead of one pa_reshape_and_cache launch, "
+                         "which is faster on MI355X; both step times are reported")
     ap.add_argument("--streams", type=int, default=1, choices=[1, 2],
                     help="chunked-prefill workloads: 2 runs decode and prefill on two streams "
                          "of equal priority (and also times the serial step)")
@@ -237,13 +242,17 @@ METRICS = {
                              "(% of bf16 MFMA peak)",
 }
 # The other workloads the default run measures after the headline one.
-# (workload, FP8 pools, shared-prefix call)
-EXTRA_WORKLOADS = [("tiny_decode", False, False), ("long_context_decode", False, False),
-                   ("prefix_sharing_decode", False, False),
-                   ("prefix_sharing_decode", False, True),
-                   ("mixed_chunked_prefill", False, False),
-                   ("llama8b_decode", True, False), ("long_context_decode", True, False),
-                   ("prefix_sharing_decode", True, False), ("mixed_chunked_prefill", True, False)]
+# (workload, FP8 pools, options of measure(), suffix of the entry's key); the
+# entries with options time the alternative entry points on the same batch.
+EXTRA_WORKLOADS = [("tiny_decode", False, {}, ""), ("long_context_decode", False, {}, ""),
+                   ("prefix_sharing_decode", False, {}, ""),
+                   ("prefix_sharing_decode", False, {"shared_prefix": True},
+                    "_shared_prefix_call"),
+                   ("mixed_chunked_prefill", False, {}, ""),
+                   ("mixed_chunked_prefill", False, {"fuse_writes": True}, "_fused_writes"),
+                   ("llama8b_decode", True, {}, ""), ("long_context_decode", True, {}, ""),
+                   ("prefix_sharing_decode", True, {}, ""),
+                   ("mixed_chunked_prefill", True, {}, "")]
 
 
 def main():
@@ -272,20 +281,20 @@ def main():
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, dev)
     result, reps = measure(case, dev, fp8, args.partition_size, args.steps, args.warmup,
-                           args.replicas, args.streams, args.shared_prefix)
+                           args.replicas, args.streams, args.shared_prefix,
+                           args.fused_writes)
     del reps
     torch.cuda.empty_cache()
     ceilings = None
     if full_run and not args.no_extra:
         result["workloads"] = {}
-        for wname, wfp8, wsp in EXTRA_WORKLOADS:
+        for wname, wfp8, opts, tag in EXTRA_WORKLOADS:
             wcase = case if wname == name else W.NAMED[wname]()
             r, wreps = measure(wcase, dev, wfp8, 0, args.steps, args.warmup, args.replicas,
-                               shared_prefix=wsp)
+                               **opts)
             del wreps
             torch.cuda.empty_cache()
-            key = wname + ("_fp8" if wfp8 else "") + ("_shared_prefix_call" if wsp else "")
-            result["workloads"][key] = summary(r)
+            result["workloads"][wname + ("_fp8" if wfp8 else "") + tag] = summary(r)
         ceilings = measure_ceilings(dev, result["roofline"]["algorithmic_bytes_per_launch"])
         result["ceilings"] = ceilings
         attach_attainable(result, ceilings)
@@ -309,7 +318,8 @@ def copy_probe(mib, dev):
     print(f"copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
-def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix=False):
+def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix=False,
+            fuse_writes=False):
     """Times `steps` steps of the hot path on one workload (after `warmup`
     untimed ones), then the same steps again with an event around each kernel
     for the per-kernel breakdown.  Returns (result dict, device replicas)."""
@@ -349,6 +359,10 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
 
     ev = {k: [] for k in ("cw0", "cw1", "dp0", "dp1", "dr1", "pf0", "pf1")}
     fused = fused_append(case)
+    # A bf16 chunked-prefill step whose decode tokens sit at L - 1: the decode
+    # tokens are written inside the decode pass (pa_decode_append) and the
+    # chunk tokens inside the prefill pass (pa_prefill_chunk_append).
+    mixed_fused = bool(fuse_writes and chunks and split_mixed(case) and not fp8 and P == 0)
     # Events of the per-kernel pass, created before it starts.
     pool = [torch.cuda.Event(enable_timing=True) for _ in range(5 * steps)]
 
@@ -365,7 +379,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         if T and fp8 and not fused:
             binding.reshape_and_cache_fp8(r.nk, r.nv, r.kc, r.vc, r.slots, FP8_K_SCALE,
                                           FP8_V_SCALE, stream=stream)
-        elif T and not fused:
+        elif T and not fused and not mixed_fused:
             binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
         if record:
             ev["dp0"].append(mark("cw1"))
@@ -383,7 +397,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         elif fp8:
             binding.decode_fp8_partitions(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL,
                                           FP8_K_SCALE, FP8_V_SCALE, ws, stream=stream)
-        elif fused:
+        elif fused or mixed_fused:
             binding.decode_append_partitions(r.out, r.q, r.nk_seq, r.nv_seq, r.kc, r.vc, r.bt,
                                              r.lens, case.scale, maxL, P, ws, stream=stream)
         else:
@@ -402,6 +416,10 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
                 binding.prefill_chunk_fp8(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens,
                                           case.scale, maxq, FP8_K_SCALE, FP8_V_SCALE,
                                           stream=stream)
+            elif mixed_fused:
+                binding.prefill_chunk_append(r.cout, r.cq, r.nk_chunk, r.nv_chunk, r.kc, r.vc,
+                                             r.cbt, r.ccu, r.clens, case.scale, maxq,
+                                             stream=stream)
             else:
                 binding.prefill_chunk(r.cout, r.cq, r.kc, r.vc, r.cbt, r.ccu, r.clens, case.scale,
                                       maxq, stream=stream)
@@ -472,6 +490,13 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
     print(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
     serial_ms = timed(lambda i: step(i, False), steps)[0] if overlap else None
+    separate_ms = None
+    if mixed_fused:  # the same step with one cache-write launch, for comparison
+        mixed_fused = False
+        for i in range(warmup):
+            step(i, False)
+        separate_ms = timed(lambda i: step(i, False), steps)[0]
+        mixed_fused = True
     plain_ms = None
     if sp:  # the same batch through the plain balanced decode, for comparison
         sp = False
@@ -494,7 +519,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         medians[a + b] = xs[len(xs) // 2]
         return sum(xs) / len(xs)
 
-    t_cw = avg_ms("cw0", "cw1") if T and not fused else None
+    t_cw = avg_ms("cw0", "cw1") if T and not fused and not mixed_fused else None
     t_dp = avg_ms("dp0", "dp1")
     t_dr = avg_ms("dp1", "dr1") if not sp else None  # inside the one call
     t_pf = avg_ms("pf0", "pf1") if chunks else None
@@ -507,6 +532,9 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
                  "decode_stream_mma_kernel" if case.dtype == "bf16" else "decode_stream_kernel")
     # The fused step's decode kernel also moves the new tokens' rows.
     dp_bytes = dec_bytes + (cw_bytes if fused else 0)
+    if mixed_fused:  # the decode tokens' rows (S of the T new rows)
+        dp_bytes = dec_bytes + acct.cache_write_bytes(S, Hkv, D, eb,
+                                                      src_elem_bytes=case.new_key.element_size())
     if sp:  # one call: prefix pass + suffix pass + reduce
         dp_kernel = "pa_decode_shared_prefix"
     result = {
@@ -529,7 +557,10 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
             "decode": ("pa_decode_shared_prefix (prefix pass, suffix pass, reduce)" if sp
                        else "pa_decode_partitions + pa_decode_reduce"),
-            "cache_write": ("fused into the decode pass (pa_decode_fp8_append)" if fused and fp8
+            "cache_write": ("decode tokens inside the decode pass (pa_decode_append), chunk "
+                            "tokens inside the prefill pass (pa_prefill_chunk_append)"
+                            if mixed_fused else
+                            "fused into the decode pass (pa_decode_fp8_append)" if fused and fp8
                             else "fused into the decode pass (pa_decode_append)" if fused
                             else "pa_reshape_and_cache_fp8" if T and fp8
                             else "pa_reshape_and_cache" if T else "none"),
@@ -543,7 +574,8 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         "new_tokens_per_s": round(S / (ms_step * 1e-3), 1),
         "serial_ms_per_step": _r(serial_ms),
         "plain_decode_ms_per_step": _r(plain_ms),
-        "kernels_ms": {"reshape_and_cache": "fused" if fused else _r(t_cw),
+        "separate_cache_write_ms_per_step": _r(separate_ms),
+        "kernels_ms": {"reshape_and_cache": "fused" if (fused or mixed_fused) else _r(t_cw),
                        ("decode_shared_prefix" if sp else "decode_partition"): _r(t_dp),
                        "decode_reduce": _r(t_dr),
                        "prefill_chunk": _r(t_pf)},
@@ -552,7 +584,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         "_kv_bytes": kv_bytes,
     }
     if chunks:
-        pf_kernel = "prefill_chunk_fp8_kernel" if fp8 else "prefill_chunk_kernel"
+        pf_kernel = "prefill_chunk_fp8_kernel" if fp8 else "prefill_chunk_kernel"  # (append variant when fused)
         pr = roofline(pf_kernel, wl, "mfma", pf_flops, t_pf, BF16_MFMA_PEAK_TFLOPS,
                       medians["pf0pf1"])
         pr["query_tokens_per_s"] = round(sum(n for n, _ in chunks) / (t_pf * 1e-3), 1)
@@ -596,7 +628,7 @@ def roofline(kernel, workload, bound, work, ms, peak, median_ms):
 def summary(r):
     """The per-workload entry of the default run's line."""
     keys = ("metric", "value", "unit", "ms_per_step", "serial_ms_per_step",
-            "plain_decode_ms_per_step", "hbm_frac",
+            "plain_decode_ms_per_step", "separate_cache_write_ms_per_step", "hbm_frac",
             "seq_tokens_per_s", "kernels_ms", "roofline", "prefill_roofline", "cache_write")
     out = {k: r[k] for k in keys if k in r}
     out["step_us"] = round(r["ms_per_step"] * 1e3, 2)

@@ -323,6 +323,32 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
                            int32_t dtype, void *stream);
 
 /*
+ * pa_prefill_chunk_append -- pa_prefill_chunk that also writes the chunks'
+ * own K/V rows into the pools inside the same pass, as pa_decode_append does
+ * for decode (the chunk's tokens are the ones a chunked-prefill step adds:
+ * "Configuring vLLM and PagedAttention ...", section "High-Throughput
+ * Batching: Continuous Batching & Chunked Prefill").
+ *
+ * new_key / new_value [Tq, Hkv, d] (bf16, device) hold the K and V rows of
+ * the query tokens: row cu_query_lens[c] + i is the token at position
+ * context_lens[c] - n_c + i of chunk c, written into slot
+ * (block_tables[c][pos / B], pos % B) -- exactly what pa_reshape_and_cache
+ * with those slots followed by pa_prefill_chunk computes and leaves in the
+ * pools.  Keys at those positions are read from new_key / new_value, so no
+ * ordering with the writes is needed; positions outside the table, or table
+ * entries outside the pool, are not written (caller errors).  Other
+ * arguments, checks and errors as pa_prefill_chunk (bf16 pools).
+ */
+pa_status pa_prefill_chunk_append(void *out, const void *query, const void *new_key,
+                                  const void *new_value, void *key_cache, void *value_cache,
+                                  const int32_t *block_tables, const int32_t *cu_query_lens,
+                                  const int32_t *context_lens, int32_t num_chunks,
+                                  int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  int32_t dtype, void *stream);
+
+/*
  * pa_copy_blocks -- copy whole KV blocks between pools: copy-on-write inside
  * the device pool, and swap of a paused request's pages to host memory and
  * back.

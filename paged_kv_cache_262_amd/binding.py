@@ -50,6 +50,8 @@ SIGNATURES = {
     "pa_prefill_chunk": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _i32, _i64, _f, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp]),
+    "pa_prefill_chunk_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _i64, _f, _i32, _vp]),
     "pa_decode_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _i32, _i64, _i32, _i32, _f, _vp, _sz, _vp]),
     "pa_decode_shared_prefix_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
@@ -419,6 +421,25 @@ def prefill_chunk(out, query, key_cache, value_cache, block_tables, cu_query_len
     C = context_lens.numel()
     _check(load().pa_prefill_chunk(
         _dev(out, "out"), _dev(query, "query"), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
+        _dev(cu_query_lens, "cu_query_lens"), _dev(context_lens, "context_lens"), C,
+        int(max_query_len), Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),
+        _dtype(query), _stream(stream)))
+    return out
+
+
+def prefill_chunk_append(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                         cu_query_lens, context_lens, scale, max_query_len, stream=None):
+    """prefill_chunk that first places the chunks' own K/V rows (new_key,
+    new_value [Tq, Hkv, D]) into their slots, inside the same pass."""
+    Tq, Hq, D = query.shape
+    NB, Hkv, B, _ = key_cache.shape
+    C = context_lens.numel()
+    if tuple(new_key.shape) != (Tq, Hkv, D) or tuple(new_value.shape) != (Tq, Hkv, D):
+        raise ValueError("new_key / new_value must be [Tq, Hkv, D]")
+    _check(load().pa_prefill_chunk_append(
+        _dev(out, "out"), _dev(query, "query"), _dev(new_key, "new_key"),
+        _dev(new_value, "new_value"), _dev(key_cache, "key_cache"),
         _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables"),
         _dev(cu_query_lens, "cu_query_lens"), _dev(context_lens, "context_lens"), C,
         int(max_query_len), Hq, Hkv, D, B, block_tables.shape[1], NB, float(scale),

@@ -12,6 +12,7 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_prefill_append.h"
 #include "pa_prefix.h"
 #include "pa_probes.h"
 
@@ -861,13 +862,20 @@ pa_status pa_decode_fp8(void *out, const void *query, const void *key_cache,
                             workspace, workspace_bytes, stream);
 }
 
-pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
-                           const void *value_cache, const int32_t *block_tables,
-                           const int32_t *cu_query_lens, const int32_t *context_lens,
-                           int32_t num_chunks, int32_t max_query_len, int32_t num_q_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                           int32_t dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and arguments shared by pa_prefill_chunk and pa_prefill_chunk_append.
+// *done is set when there is nothing to launch.
+pa_status setup_prefill(pa::PrefillArgs &a, bool *done, void *out, const void *query,
+                        const void *key_cache, const void *value_cache,
+                        const int32_t *block_tables, const int32_t *cu_query_lens,
+                        const int32_t *context_lens, int32_t num_chunks, int32_t max_query_len,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                        float scale, int32_t dtype, void *stream) {
+    *done = true;
     if (dtype != PA_BF16)
         return fail(PA_ERR_UNSUPPORTED, "prefill runs on bf16 matrix cores: dtype must be bf16");
     pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
@@ -895,7 +903,6 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
                                           num_blocks, (hipStream_t)stream);
         if (d != PA_OK) return d;
     }
-    pa::PrefillArgs a;
     a.out = out;
     a.query = query;
     a.key_cache = key_cache;
@@ -915,7 +922,50 @@ pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
     a.kv_fp8 = 0;
     a.k_scale = 1.0f;
     a.v_scale = 1.0f;
+    *done = false;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_prefill_chunk(void *out, const void *query, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *cu_query_lens, const int32_t *context_lens,
+                           int32_t num_chunks, int32_t max_query_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           int32_t dtype, void *stream) {
+    pa::PrefillArgs a;
+    bool done;
+    const pa_status s = setup_prefill(a, &done, out, query, key_cache, value_cache, block_tables,
+                                      cu_query_lens, context_lens, num_chunks, max_query_len,
+                                      num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, num_blocks, scale, dtype, stream);
+    if (s != PA_OK || done) return s;
     return hip_status(pa::launch_prefill_chunk(a, (hipStream_t)stream), "prefill_chunk");
+}
+
+pa_status pa_prefill_chunk_append(void *out, const void *query, const void *new_key,
+                                  const void *new_value, void *key_cache, void *value_cache,
+                                  const int32_t *block_tables, const int32_t *cu_query_lens,
+                                  const int32_t *context_lens, int32_t num_chunks,
+                                  int32_t max_query_len, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                  int32_t dtype, void *stream) {
+    pa::PrefillArgs a;
+    bool done;
+    const pa_status s = setup_prefill(a, &done, out, query, key_cache, value_cache, block_tables,
+                                      cu_query_lens, context_lens, num_chunks, max_query_len,
+                                      num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, num_blocks, scale, dtype, stream);
+    if (s != PA_OK || done) return s;
+    CHECK_PTR(new_key, 16);
+    CHECK_PTR(new_value, 16);
+    return hip_status(pa::launch_prefill_chunk_append(a, new_key, new_value, (hipStream_t)stream),
+                      "prefill_chunk_append");
 }
 
 pa_status pa_prefill_chunk_fp8(void *out, const void *query, const void *key_cache,

@@ -39,6 +39,7 @@
 // ds_read_b64_tr_b16, 4 keys of one dim per read.
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_prefill_append.h"
 
 namespace pa {
 
@@ -137,13 +138,21 @@ struct KvLds {
     }
 };
 
-template <int D, int B, int G>
+// AP (append): new_key / new_value [Tq][Hkv][D] hold the K/V rows of the
+// chunks' own tokens (row q_begin + i: position L - n + i of chunk c).  Keys
+// at those positions are staged from these rows instead of the pools, and
+// every workgroup writes the rows of its own queries (for its kv head) into
+// their slots, so the pass needs no cache write before it and no workgroup
+// reads a slot another one writes.
+template <int D, int B, int G, bool AP>
 __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     bf16_t *__restrict__ out, const bf16_t *__restrict__ query,
     const bf16_t *__restrict__ key_cache, const bf16_t *__restrict__ value_cache,
     const int32_t *__restrict__ block_tables, const int32_t *__restrict__ cu_query_lens,
     const int32_t *__restrict__ context_lens, int num_q_heads, int num_kv_heads, int max_blocks,
-    int64_t num_blocks, float scale_log2, int num_tiles, int total) {
+    int64_t num_blocks, float scale_log2, int num_tiles, int total,
+    const bf16_t *__restrict__ new_key, const bf16_t *__restrict__ new_value,
+    bf16_t *key_dst, bf16_t *value_dst) {
     using LY = KvLds<D>;
     constexpr int QT = kPfRows / G;  // queries per tile
     constexpr int KS = D / 32;       // k-steps of S^T = K Q^T
@@ -180,6 +189,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     const int pos0 = L - n + q0;                    // position of the tile's first query
     const int kend = min(L, pos0 + nq);             // keys any row of the tile may see
     const int32_t *bt = block_tables + (int64_t)c * max_blocks;
+    const int new0 = L - n;                         // AP: first position of the chunk's rows
 
     const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
@@ -280,7 +290,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
             const int kb = 2 * pr + bp;
             if (kb >= nkb) continue;  // block past the tile's keys
             lds_void *dst = (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024);
-            if (kb * kKeyBlock + kKeyBlock <= kend) {
+            if (kb * kKeyBlock + kKeyBlock <= (AP ? min(kend, new0) : kend)) {
                 const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)seg_addr, j);
                 const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(seg_addr >> 32), j);
                 const char *page = (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
@@ -289,12 +299,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
             } else {
                 const int kk = s * LY::KPS + seg_row;
                 const int key = min(kb * kKeyBlock + kk, kend - 1);
-                int phys = bt_s[key / B - win_p0];
-                if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;
-                const char *pool = (const char *)(tensor ? value_cache : key_cache);
-                const char *src = pool + ((int64_t)phys * block_elems +
-                                          ((int64_t)g * B + key % B) * D) * 2 +
-                                  ((seg_ch ^ LY::swz(kk)) << 4);
+                const char *src;
+                if (AP && key >= new0) {  // one of the chunk's own rows
+                    const bf16_t *rows = tensor ? new_value : new_key;
+                    src = (const char *)(rows + ((int64_t)(q_begin + key - new0) * num_kv_heads +
+                                                 g) * D) +
+                          ((seg_ch ^ LY::swz(kk)) << 4);
+                } else {
+                    int phys = bt_s[key / B - win_p0];
+                    if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;
+                    const char *pool = (const char *)(tensor ? value_cache : key_cache);
+                    src = pool + ((int64_t)phys * block_elems + ((int64_t)g * B + key % B) * D) * 2 +
+                          ((seg_ch ^ LY::swz(kk)) << 4);
+                }
                 __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
             }
         }
@@ -475,6 +492,25 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     for (int pr = 0; pr < npairs; pr += 2) {
         step(stage_a, stage_b, pr);
         if (pr + 1 < npairs) step(stage_b, stage_a, pr + 1);
+    }
+    if (AP) {
+        // The K and V rows of this tile's queries (kv head g) into their
+        // slots: nq rows of NCH 16-byte chunks per tensor.  Positions before
+        // 0 or past the table have no slot; an entry outside the pool is a
+        // caller error and is skipped.
+        constexpr int NCH = D * 2 / 16;
+        for (int t = tid; t < 2 * nq * NCH; t += kPfWaves * 64) {
+            const int tensor = t / (nq * NCH), r = (t / NCH) % nq, ch = t % NCH;
+            const int pos = pos0 + r;
+            if (pos < 0 || pos >= max_tokens) continue;
+            const int phys = bt[pos / B];
+            if (phys < 0 || (int64_t)phys >= num_blocks) continue;
+            const int64_t row = (int64_t)(q_begin + q0 + r) * num_kv_heads + g;
+            const u32x4 v = *(const u32x4 *)((tensor ? new_value : new_key) + row * D + ch * 8);
+            bf16_t *dstp = (tensor ? value_dst : key_dst) +
+                           ((int64_t)phys * block_elems + ((int64_t)g * B + pos % B) * D) + ch * 8;
+            *(u32x4 *)dstp = v;
+        }
     }
     __syncthreads();  // every wave is done with both stages
 
@@ -911,7 +947,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
 }
 
 template <int D, int B, int G>
-static hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
+static hipError_t launch(const PrefillArgs &a, hipStream_t stream, const void *new_key,
+                         const void *new_value) {
     constexpr int QT = kPfRows / G;
     const int tiles = cdiv(a.max_query_len, QT);
     const int64_t total = (int64_t)tiles * a.num_kv_heads * a.num_chunks;
@@ -926,30 +963,45 @@ static hipError_t launch(const PrefillArgs &a, hipStream_t stream) {
                            (int)total);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, B, G>), dim3((unsigned)total), dim3(kPfWaves * 64),
-                       0, stream, (bf16_t *)a.out, (const bf16_t *)a.query,
-                       (const bf16_t *)a.key_cache, (const bf16_t *)a.value_cache, a.block_tables,
-                       a.cu_query_lens, a.context_lens, a.num_q_heads, a.num_kv_heads,
-                       a.max_blocks_per_seq, a.num_blocks, a.scale * kLog2e, tiles, (int)total);
+    if (new_key)
+        hipLaunchKernelGGL((prefill_chunk_kernel<D, B, G, true>), dim3((unsigned)total),
+                           dim3(kPfWaves * 64), 0, stream, (bf16_t *)a.out,
+                           (const bf16_t *)a.query, (const bf16_t *)a.key_cache,
+                           (const bf16_t *)a.value_cache, a.block_tables, a.cu_query_lens,
+                           a.context_lens, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
+                           a.num_blocks, a.scale * kLog2e, tiles, (int)total,
+                           (const bf16_t *)new_key, (const bf16_t *)new_value,
+                           (bf16_t *)a.key_cache, (bf16_t *)a.value_cache);
+    else
+        hipLaunchKernelGGL((prefill_chunk_kernel<D, B, G, false>), dim3((unsigned)total),
+                           dim3(kPfWaves * 64), 0, stream, (bf16_t *)a.out,
+                           (const bf16_t *)a.query, (const bf16_t *)a.key_cache,
+                           (const bf16_t *)a.value_cache, a.block_tables, a.cu_query_lens,
+                           a.context_lens, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
+                           a.num_blocks, a.scale * kLog2e, tiles, (int)total,
+                           (const bf16_t *)nullptr, (const bf16_t *)nullptr, (bf16_t *)nullptr,
+                           (bf16_t *)nullptr);
     return hipGetLastError();
 }
 
 template <int D, int B>
-static hipError_t by_group(const PrefillArgs &a, hipStream_t stream) {
+static hipError_t by_group(const PrefillArgs &a, hipStream_t stream, const void *nk,
+                           const void *nv) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch<D, B, 1>(a, stream);
-        case 2: return launch<D, B, 2>(a, stream);
-        case 4: return launch<D, B, 4>(a, stream);
-        case 8: return launch<D, B, 8>(a, stream);
+        case 1: return launch<D, B, 1>(a, stream, nk, nv);
+        case 2: return launch<D, B, 2>(a, stream, nk, nv);
+        case 4: return launch<D, B, 4>(a, stream, nk, nv);
+        case 8: return launch<D, B, 8>(a, stream, nk, nv);
     }
     return hipErrorNotSupported;
 }
 
 template <int D>
-static hipError_t by_block(const PrefillArgs &a, hipStream_t stream) {
+static hipError_t by_block(const PrefillArgs &a, hipStream_t stream, const void *nk,
+                           const void *nv) {
     switch (a.block_size) {
-        case 16: return by_group<D, 16>(a, stream);
-        case 32: return by_group<D, 32>(a, stream);
+        case 16: return by_group<D, 16>(a, stream, nk, nv);
+        case 32: return by_group<D, 32>(a, stream, nk, nv);
     }
     return hipErrorNotSupported;
 }
@@ -961,8 +1013,18 @@ bool prefill_shape_supported(int head_dim, int block_size, int group) {
 
 hipError_t launch_prefill_chunk(const PrefillArgs &a, hipStream_t stream) {
     switch (a.head_dim) {
-        case 64: return by_block<64>(a, stream);
-        case 128: return by_block<128>(a, stream);
+        case 64: return by_block<64>(a, stream, nullptr, nullptr);
+        case 128: return by_block<128>(a, stream, nullptr, nullptr);
+    }
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_prefill_chunk_append(const PrefillArgs &a, const void *new_key,
+                                       const void *new_value, hipStream_t stream) {
+    if (a.kv_fp8 || !new_key || !new_value) return hipErrorNotSupported;
+    switch (a.head_dim) {
+        case 64: return by_block<64>(a, stream, new_key, new_value);
+        case 128: return by_block<128>(a, stream, new_key, new_value);
     }
     return hipErrorNotSupported;
 }
