@@ -740,7 +740,8 @@ pa_status pa_reshape_and_cache_fp8(const void *key, const void *value, void *key
                                    int32_t block_size, int64_t num_blocks, int32_t dtype,
                                    float k_scale, float v_scale, void *stream) {
     if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
-    if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads <= 0");
+    if (num_kv_heads <= 0 || num_kv_heads > 65535)
+        return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
     if (dtype != PA_F32 && dtype != PA_BF16)
         return fail(PA_ERR_UNSUPPORTED, "dtype %d of the new rows not supported", dtype);
     if ((head_dim != 64 && head_dim != 128) || (block_size != 16 && block_size != 32))

@@ -75,34 +75,92 @@ __device__ __forceinline__ void load4(const T *p, float (&x)[4]) {
     }
 }
 
-// One workgroup per new token; a thread takes 4 consecutive dims of one kv
-// head: one 4-byte store into the K row, four byte stores down the dims of
-// the transposed V page.
+template <typename T>
+__device__ __forceinline__ float load1(const T *p) {
+    if constexpr (sizeof(T) == 4)
+        return *p;
+    else
+        return __uint_as_float((uint32_t)*(const uint16_t *)p << 16);
+}
+
+// One workgroup per (group of kFp8Group consecutive new tokens, kv head).
+// When the group's slots are kFp8Group consecutive slots starting at a
+// multiple of kFp8Group (a chunk's tokens filling that part of a block), the
+// group's V codes of one dim form one 16-byte segment of a transposed V page
+// row, written whole, and its K rows are contiguous, so every store of the
+// workgroup covers whole 16-byte pieces.  Otherwise each token of the group is
+// written on its own: a thread takes 4 consecutive dims, one 4-byte store into
+// the K row and four byte stores down the dims of the V page (each lands in
+// its own row of the page).
+constexpr int kFp8Group = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
     const T *__restrict__ key, const T *__restrict__ value, uint8_t *__restrict__ key_cache,
-    uint8_t *__restrict__ value_cache, const int64_t *__restrict__ slot_mapping, int num_kv_heads,
-    int head_dim, int block_size, int64_t num_slots, float k_inv, float v_inv) {
-    const int t = blockIdx.x;
-    const int64_t slot = slot_mapping[t];
-    if (slot < 0 || slot >= num_slots) return;  // padding (or a caller error)
-    const int64_t blk = slot / block_size;
-    const int off = (int)(slot - blk * block_size);
-    const int quads = head_dim / 4;
-    for (int i = threadIdx.x; i < num_kv_heads * quads; i += blockDim.x) {
-        const int h = i / quads, d0 = (i - h * quads) * 4;
-        const int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + d0;
-        const int64_t page = (blk * num_kv_heads + h) * (int64_t)block_size * head_dim;
+    uint8_t *__restrict__ value_cache, const int64_t *__restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, int head_dim, int block_size, int64_t num_slots, float k_inv,
+    float v_inv) {
+    __shared__ int64_t sl[kFp8Group];
+    const int t0 = blockIdx.x * kFp8Group, h = blockIdx.y;
+    const int nt = min(kFp8Group, num_tokens - t0);
+    if (threadIdx.x < kFp8Group) sl[threadIdx.x] = threadIdx.x < nt ? slot_mapping[t0 + threadIdx.x] : -1;
+    __syncthreads();
+    const int64_t s0 = sl[0];
+    bool full = nt == kFp8Group && s0 >= 0 && s0 + kFp8Group <= num_slots && s0 % kFp8Group == 0;
+#pragma unroll
+    for (int i = 1; i < kFp8Group; ++i) full = full && sl[i] == s0 + i;
+    const int D = head_dim, B = block_size;
+    if (full) {
+        // The group lies in one block (block size is a multiple of 16), at
+        // offsets off0 .. off0 + 15.  Lanes 4d .. 4d + 3 encode the 16 codes
+        // of V row d (4 tokens each) and store them as one contiguous 16-byte
+        // piece; consecutive lanes cover consecutive 4-byte pieces of the
+        // group's K rows, which are contiguous in the page.
+        const int64_t blk = s0 / B;
+        const int off0 = (int)(s0 - blk * B);
+        const int64_t page = (blk * num_kv_heads + h) * (int64_t)B * D;
+        const int64_t row0 = (int64_t)t0 * num_kv_heads + h;  // row of token t0, head h
+        for (int j = threadIdx.x; j < 4 * D; j += blockDim.x) {
+            const int d = j >> 2, q = j & 3;
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = load1(value + (row0 + (int64_t)(4 * q + e) * num_kv_heads) * D + d);
+                w |= e4m3_code(x * v_inv) << (8 * e);
+            }
+            *(uint32_t *)(value_cache + page + (int64_t)d * B + off0 + 4 * q) = w;
+        }
+        const int quads = D / 4;
+        for (int j = threadIdx.x; j < kFp8Group * quads; j += blockDim.x) {
+            const int i = j / quads, d0 = (j - i * quads) * 4;
+            float k[4];
+            load4(key + (row0 + (int64_t)i * num_kv_heads) * D + d0, k);
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w |= e4m3_code(k[e] * k_inv) << (8 * e);
+            *(uint32_t *)(key_cache + page + (int64_t)(off0 + i) * D + d0) = w;
+        }
+        return;
+    }
+    const int quads = D / 4;
+    for (int j = threadIdx.x; j < nt * quads; j += blockDim.x) {
+        const int i = j / quads, d0 = (j - i * quads) * 4;
+        const int64_t slot = sl[i];
+        if (slot < 0 || slot >= num_slots) continue;  // padding (or a caller error)
+        const int64_t blk = slot / B;
+        const int off = (int)(slot - blk * B);
+        const int64_t src = ((int64_t)(t0 + i) * num_kv_heads + h) * D + d0;
+        const int64_t page = (blk * num_kv_heads + h) * (int64_t)B * D;
         float k[4], v[4];
         load4(key + src, k);
         load4(value + src, v);
         uint32_t kw = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) kw |= e4m3_code(k[e] * k_inv) << (8 * e);
-        *(uint32_t *)(key_cache + page + (int64_t)off * head_dim + d0) = kw;
+        *(uint32_t *)(key_cache + page + (int64_t)off * D + d0) = kw;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            value_cache[page + (int64_t)(d0 + e) * block_size + off] = (uint8_t)e4m3_code(v[e] * v_inv);
+            value_cache[page + (int64_t)(d0 + e) * B + off] = (uint8_t)e4m3_code(v[e] * v_inv);
     }
 }
 
@@ -111,20 +169,20 @@ hipError_t launch_reshape_and_cache_fp8(const void *key, const void *value, void
                                         int num_tokens, int num_kv_heads, int head_dim,
                                         int block_size, int64_t num_blocks, int elem_bytes,
                                         float k_inv_scale, float v_inv_scale, hipStream_t stream) {
-    const int per_token = num_kv_heads * head_dim / 4;
-    const int threads = per_token >= 256 ? 256 : ((per_token + 63) / 64) * 64;
+    if (num_tokens == 0) return hipSuccess;
+    const dim3 grid((unsigned)((num_tokens + kFp8Group - 1) / kFp8Group), (unsigned)num_kv_heads);
     if (elem_bytes == 4)
-        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, dim3(num_tokens), dim3(threads), 0,
-                           stream, (const float *)key, (const float *)value,
-                           (uint8_t *)key_cache, (uint8_t *)value_cache, slot_mapping,
-                           num_kv_heads, head_dim, block_size, num_blocks * block_size,
-                           k_inv_scale, v_inv_scale);
+        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<float>, grid, dim3(256), 0, stream,
+                           (const float *)key, (const float *)value, (uint8_t *)key_cache,
+                           (uint8_t *)value_cache, slot_mapping, num_tokens, num_kv_heads,
+                           head_dim, block_size, num_blocks * block_size, k_inv_scale,
+                           v_inv_scale);
     else
-        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, dim3(num_tokens), dim3(threads),
-                           0, stream, (const bf16_t *)key, (const bf16_t *)value,
-                           (uint8_t *)key_cache, (uint8_t *)value_cache, slot_mapping,
-                           num_kv_heads, head_dim, block_size, num_blocks * block_size,
-                           k_inv_scale, v_inv_scale);
+        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<bf16_t>, grid, dim3(256), 0, stream,
+                           (const bf16_t *)key, (const bf16_t *)value, (uint8_t *)key_cache,
+                           (uint8_t *)value_cache, slot_mapping, num_tokens, num_kv_heads,
+                           head_dim, block_size, num_blocks * block_size, k_inv_scale,
+                           v_inv_scale);
     return hipGetLastError();
 }
 

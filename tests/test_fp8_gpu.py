@@ -553,6 +553,33 @@ def test_fp8_cache_write_runs_of_consecutive_slots(dtype, B):
     assert torch.equal(gv.cpu(), rv), "V pool differs"
 
 
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("bf16", 32), ("f32", 16), ("f32", 32)])
+def test_fp8_cache_write_whole_row_groups(dtype, B):
+    """A chunk's 317 new tokens at positions 16 .. 332, so groups of 16
+    consecutive tokens start at 16-aligned slots and take the whole-row path;
+    one group has a padding token, one a foreign slot, one two of its slots
+    swapped (all three fall back to per-token writes), and the last group is
+    partial: bit-exact against the oracle."""
+    c = W.make_case("fp8 groups", 315, dtype, 8, 4, 128, B, [1], chunks=[(317, 333)],
+                    extra_blocks=2)
+    slots = c.slot_mapping[-317:].clone()             # the chunk's own positions 16 .. 332
+    nk, nv = c.new_key[-317:].contiguous(), c.new_value[-317:].contiguous()
+    assert int(slots[0]) % 16 == 0
+    slots[37] = -1                                    # padding inside group 2
+    slots[70] = int(c.block_tables[0, 0]) * B         # the decode sequence's slot, group 4
+    a, b = int(slots[90]), int(slots[91])             # group 5: two slots swapped
+    slots[90], slots[91] = b, a
+    ks, vs = 0.05, 1.0 / 16
+    kc8, vc8 = fp8_pools(c, ks, vs)
+    say("fp8 cache write whole-row groups", dtype, B)
+    gk, gv = dev(kc8), dev(vc8)
+    binding.reshape_and_cache_fp8(dev(nk), dev(nv), gk, gv, dev(slots), ks, vs)
+    torch.cuda.synchronize()
+    rk, rv = oracle.reshape_and_cache_fp8(nk, nv, kc8, vc8, slots, ks, vs)
+    assert torch.equal(gk.cpu(), rk), "K pool differs"
+    assert torch.equal(gv.cpu(), rv), "V pool differs"
+
+
 def test_fp8_block_manager_drives_decode():
     """The host block manager drives FP8 decode steps: prompts sharing a system
     prefix (reused through the prefix cache), a fork whose first write copies
