@@ -96,13 +96,16 @@ def parse():
 KERNEL_SOURCES = {
     "reshape_and_cache_kernel": ["reshape_and_cache.hip", "pa_common.h", "pa_internal.h"],
     "reshape_and_cache_fp8_kernel": ["reshape_and_cache.hip", "pa_common.h", "pa_internal.h"],
-    "decode_stream_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
-    "decode_stream_fp8_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
-    "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
-    "decode_stream_reduce_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
-    "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h"],
-    "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
-    "prefill_chunk_fp8_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h"],
+    "decode_stream_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h", "pa_prefix.h"],
+    "decode_stream_fp8_kernel": ["decode.hip", "pa_common.h", "pa_internal.h", "pa_prefix.h"],
+    "decode_stream_kernel": ["decode.hip", "pa_common.h", "pa_internal.h", "pa_prefix.h"],
+    "decode_stream_reduce_kernel": ["decode.hip", "pa_common.h", "pa_internal.h", "pa_prefix.h"],
+    "decode_partition_kernel": ["decode.hip", "pa_common.h", "pa_internal.h", "pa_prefix.h"],
+    "decode_prefix_mma_kernel": ["decode.hip", "pa_common.h", "pa_internal.h", "pa_prefix.h"],
+    "prefill_chunk_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h", "pa_prefill_append.h"],
+    "prefill_chunk_fp8_kernel": ["prefill.hip", "pa_common.h", "pa_internal.h",
+                                 "pa_prefill_append.h"],
+    "copy_blocks_kernel": ["copy_blocks.hip", "pa_common.h", "pa_internal.h"],
 }
 
 

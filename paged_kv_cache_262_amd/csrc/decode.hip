@@ -1520,7 +1520,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
 // memory round trips rather than one per record.  x_n <= 8 further records
 // (x_ml + 2k, x_o + k * D; the shared-prefix records) join the merge; nrec
 // may then be 0.
-template <typename T, int D>
+template <typename T, int D, bool XR = false>
 __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *__restrict__ ml,
                                               int64_t ml_stride, const float *__restrict__ o,
                                               int64_t o_stride, int nrec, int lane,
@@ -1532,19 +1532,21 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
     float2 w0 = make_float2(NEG_INF, 0.f);
     if (lane < nrec) w0 = *(const float2 *)(ml + lane * ml_stride);
     float2 xw = make_float2(NEG_INF, 0.f);
-    if (lane < x_n) xw = *(const float2 *)(x_ml + 2 * lane);
+    if (XR && lane < x_n) xw = *(const float2 *)(x_ml + 2 * lane);
     // The outputs of the first 8 records go out with the weights (they do not
     // depend on them), so a row of up to 8 records costs one round trip.
-    vecd v0[8], xv[8];
-    if (nrec > 0) {
+    vecd v0[8], xv[XR ? 8 : 1];
+    if (!XR || nrec > 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             v0[j] = *(const vecd *)(o + min(j, nrec - 1) * o_stride + lane * DPL);
     }
+    if constexpr (XR) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (j < x_n) xv[j] = *(const vecd *)(x_o + (int64_t)j * D + lane * DPL);
-    float M = fmaxf(w0.x, xw.x);
+        for (int j = 0; j < 8; ++j)
+            if (j < x_n) xv[j] = *(const vecd *)(x_o + (int64_t)j * D + lane * DPL);
+    }
+    float M = XR ? fmaxf(w0.x, xw.x) : w0.x;
     for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, ml[k * ml_stride]);
     M = wave_max(M);
     float lsum = 0.f;
@@ -1572,7 +1574,7 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
             }
         }
     }
-    if (x_n > 0) {
+    if constexpr (XR) {
         const float fx = (xw.x == NEG_INF) ? 0.f : fast_exp2(xw.x - M);  // 0 past x_n
         lsum = fmaf(fx, xw.y, lsum);
 #pragma unroll
@@ -1593,9 +1595,10 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
 // Merge the partial records of each (sequence, q head): records of pair i
 // come from waves wave_of_unit(first unit) .. wave_of_unit(last unit), stored
 // at record i + wave.  One wave per output row.
-// x_n > 0: every row also merges its x_n shared-prefix records (x_o [row][x_n][D],
-// x_ml [row][x_n][2]), and the decode kernel wrote every pair as records.
-template <typename T, int D>
+// XR: every row also merges its x_n (1 .. 8) shared-prefix records (x_o
+// [row][x_n][D], x_ml [row][x_n][2]), and the decode kernel wrote every pair
+// as records.
+template <typename T, int D, bool XR>
 __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     T *__restrict__ out, const int *__restrict__ ws_scan, int S, int num_q_heads,
     int num_kv_heads, int nw, const float *__restrict__ rec_o, const float *__restrict__ rec_ml,
@@ -1608,11 +1611,11 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     const int G = num_q_heads / num_kv_heads;
     const int g = h / G, hh = h - g * G;
     const int us = ws_scan[s + 1] - ws_scan[s];
-    const float *xo = x_n > 0 ? x_o + row * x_n * D : nullptr;
-    const float *xml = x_n > 0 ? x_ml + row * x_n * 2 : nullptr;
+    const float *xo = XR ? x_o + row * x_n * D : nullptr;
+    const float *xml = XR ? x_ml + row * x_n * 2 : nullptr;
     if (us == 0) {
-        if (x_n > 0) {
-            merge_records<T, D>(out + row * D, nullptr, 0, nullptr, 0, 0, lane, xml, xo, x_n);
+        if (XR) {
+            merge_records<T, D, XR>(out + row * D, nullptr, 0, nullptr, 0, 0, lane, xml, xo, x_n);
             return;
         }
 #pragma unroll
@@ -1623,11 +1626,11 @@ __global__ __launch_bounds__(256) void decode_stream_reduce_kernel(
     const int nwe = (int)min((int64_t)nw, U);  // the waves that worked (us > 0, so U > 0)
     const int64_t u0 = (int64_t)ws_scan[s] * num_kv_heads + (int64_t)g * us;
     const int w0 = wave_of_unit(u0, U, nwe), w1 = wave_of_unit(u0 + us - 1, U, nwe);
-    if (w0 == w1 && x_n == 0) return;  // finished by its wave
+    if (w0 == w1 && !XR) return;  // finished by its wave
     const int64_t item = (int64_t)s * num_kv_heads + g;
     const int64_t rid0 = (item + w0) * G + hh;
-    merge_records<T, D>(out + row * D, rec_ml + rid0 * 2, 2 * G, rec_o + rid0 * D, (int64_t)G * D,
-                        w1 - w0 + 1, lane, xml, xo, x_n);
+    merge_records<T, D, XR>(out + row * D, rec_ml + rid0 * 2, 2 * G, rec_o + rid0 * D,
+                            (int64_t)G * D, w1 - w0 + 1, lane, xml, xo, x_n);
 }
 
 // ---------------------------------------------------------------------------
@@ -1932,11 +1935,15 @@ template <typename T, int D>
 static hipError_t launch_red(const DecodeArgs &a, hipStream_t stream,
                              const PrefixArgs *px = nullptr) {
     const unsigned blocks = (unsigned)cdiv((int)((int64_t)a.num_seqs * a.num_q_heads), 4);
-    if (a.stream_waves > 0) {
-        hipLaunchKernelGGL((decode_stream_reduce_kernel<T, D>), dim3(blocks), dim3(256), 0,
+    if (a.stream_waves > 0 && px) {
+        hipLaunchKernelGGL((decode_stream_reduce_kernel<T, D, true>), dim3(blocks), dim3(256), 0,
                            stream, (T *)a.out, a.ws_scan, a.num_seqs, a.num_q_heads,
-                           a.num_kv_heads, a.stream_waves, a.ws_o, a.ws_ml,
-                           px ? px->x_o : nullptr, px ? px->x_ml : nullptr, px ? px->ksplit : 0);
+                           a.num_kv_heads, a.stream_waves, a.ws_o, a.ws_ml, px->x_o, px->x_ml,
+                           px->ksplit);
+    } else if (a.stream_waves > 0) {
+        hipLaunchKernelGGL((decode_stream_reduce_kernel<T, D, false>), dim3(blocks), dim3(256), 0,
+                           stream, (T *)a.out, a.ws_scan, a.num_seqs, a.num_q_heads,
+                           a.num_kv_heads, a.stream_waves, a.ws_o, a.ws_ml, nullptr, nullptr, 0);
     } else {
         hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3(blocks), dim3(256), 0, stream,
                            (T *)a.out, a.context_lens, a.num_seqs, a.num_q_heads, max_tokens(a),
