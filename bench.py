@@ -73,10 +73,9 @@ def parse():
                          "pa_copy_blocks on the workload's pool")
     ap.add_argument("--copy-seqs", type=int, default=8,
                     help="sequences whose blocks a copy op moves")
-    ap.add_argument("--shared-prefix", action="store_true",
-                    help="prefix-sharing workload: pa_decode_shared_prefix (prefix pass, "
-                         "suffix pass, reduce) instead of the plain decode, which is faster "
-                         "on MI355X; both step times are reported")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="prefix-sharing workload: the plain decode instead of "
+                         "pa_decode_shared_prefix (whose step also reports the plain one)")
     ap.add_argument("--fused-writes", action="store_true",
                     help="chunked-prefill workloads (bf16): write the new tokens inside the "
                          "decode pass (pa_decode_append) and the prefill pass "
@@ -249,8 +248,6 @@ METRICS = {
 # entries with options time the alternative entry points on the same batch.
 EXTRA_WORKLOADS = [("tiny_decode", False, {}, ""), ("long_context_decode", False, {}, ""),
                    ("prefix_sharing_decode", False, {}, ""),
-                   ("prefix_sharing_decode", False, {"shared_prefix": True},
-                    "_shared_prefix_call"),
                    ("mixed_chunked_prefill", False, {}, ""),
                    ("mixed_chunked_prefill", False, {"fuse_writes": True}, "_fused_writes"),
                    ("llama8b_decode", True, {}, ""), ("long_context_decode", True, {}, ""),
@@ -284,7 +281,7 @@ def main():
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib, dev)
     result, reps = measure(case, dev, fp8, args.partition_size, args.steps, args.warmup,
-                           args.replicas, args.streams, args.shared_prefix,
+                           args.replicas, args.streams, not args.no_shared_prefix,
                            args.fused_writes)
     del reps
     torch.cuda.empty_cache()
@@ -321,7 +318,7 @@ def copy_probe(mib, dev):
     print(f"copy probe: {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
 
 
-def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix=False,
+def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix=True,
             fuse_writes=False):
     """Times `steps` steps of the hot path on one workload (after `warmup`
     untimed ones), then the same steps again with an event around each kernel
@@ -337,7 +334,8 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
     ws = binding.make_workspace(reps[0].q, reps[0].kc, maxL, P)
     stream = torch.cuda.current_stream()
     # The prefix-sharing batch (bf16): pa_decode_shared_prefix, which reads the
-    # shared blocks once per tile of sequences instead of once per sequence.
+    # shared blocks once per tile of sequences instead of once per sequence
+    # (its prefix pass runs on a second stream beside the suffix pass).
     pb = case.shared_blocks.numel() if case.shared_blocks is not None else 0
     sp = bool(shared_prefix and pb and not fp8 and case.dtype == "bf16" and P == 0)
     ws_sp = binding.make_shared_prefix_workspace(reps[0].q, reps[0].kc, maxL, pb) if sp else None

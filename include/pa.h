@@ -211,6 +211,15 @@ size_t pa_decode_no_alloc_max_workspace(void);
  * log-sum-exp rescaling.  A sequence with context_lens[s] <= prefix_blocks *
  * block_size attends to its own first context_lens[s] tokens only.
  *
+ * The prefix pass runs on a stream the library creates for the current
+ * device (default priority, on the first call on that device, kept until the
+ * process ends), forked from `stream` and joined back into it with events
+ * before the reduce, so it runs beside the suffix pass; the current device
+ * must be the device of `stream`.  Everything the call enqueues is ordered
+ * after earlier work on `stream`, and later work on `stream` waits for all of
+ * it.  Calls from several host threads may overlap (their enqueue sequences
+ * are serialised).
+ *
  * Arguments as pa_decode, plus prefix_blocks in [0, max_blocks_per_seq]
  * (0: the plain balanced decode); num_seqs at most 8192 (else
  * PA_ERR_UNSUPPORTED); workspace (256-byte aligned) of at least

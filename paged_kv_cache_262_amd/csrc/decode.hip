@@ -977,6 +977,10 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
 // those of decode_stream_mma_kernel.
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+// Unit buffers of the prefix pass: two keep it at 188 + 40 registers and
+// 32 KiB of LDS per workgroup, so one of its workgroups fits on a CU beside
+// one of the suffix pass (the two run on separate streams at once).
+constexpr int kPrefixBuffers = 2;
 
 template <int D, int B, int G, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_prefix_mma_kernel(
@@ -986,7 +990,7 @@ __global__ __launch_bounds__(NW * 64) void decode_prefix_mma_kernel(
     int64_t num_blocks, int prefix_tokens, int ksplit, float scale_log2, float *__restrict__ x_o,
     float *__restrict__ x_ml) {
     constexpr int ROWB = D * 2, NCH = ROWB / 16, KS = D / 32, DT = D / 16;
-    constexpr int UNIT_BYTES = kUnitTokens * ROWB, NB = kMmaBuffers;
+    constexpr int UNIT_BYTES = kUnitTokens * ROWB, NB = kPrefixBuffers;
     constexpr int KPS = 1024 / ROWB;               // rows per 1 KB DMA segment
     constexpr int SEGS = UNIT_BYTES / 1024;        // DMA instructions per unit
     constexpr int CPW = 16 / G;                    // sequences per wave
@@ -1517,9 +1521,9 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
 // split softmax results).  Record k's (m, l) pair is at ml + k * ml_stride, its
 // output at o + k * o_stride.  Lane k loads the weights of record k, and the
 // outputs of 8 records are loaded before any is used, so a row costs a few
-// memory round trips rather than one per record.  x_n <= 8 further records
-// (x_ml + 2k, x_o + k * D; the shared-prefix records) join the merge; nrec
-// may then be 0.
+// memory round trips rather than one per record.  XR: x_n further records
+// (x_ml + 2k, x_o + k * D; the shared-prefix records) follow the nrec ones
+// as records nrec .. nrec + x_n - 1; nrec may then be 0.
 template <typename T, int D, bool XR = false>
 __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *__restrict__ ml,
                                               int64_t ml_stride, const float *__restrict__ o,
@@ -1529,43 +1533,42 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
                                               int x_n = 0) {
     constexpr int DPL = D / 64;  // dims per lane
     typedef float vecd __attribute__((ext_vector_type(DPL)));
+    const int nall = XR ? nrec + x_n : nrec;
+    auto ml_at = [&](int k) __attribute__((always_inline)) -> const float * {
+        if (XR && k >= nrec) return x_ml + 2 * (k - nrec);
+        return ml + k * ml_stride;
+    };
+    auto o_at = [&](int k) __attribute__((always_inline)) -> const float * {
+        if (XR && k >= nrec) return x_o + (int64_t)(k - nrec) * D;
+        return o + k * o_stride;
+    };
     float2 w0 = make_float2(NEG_INF, 0.f);
-    if (lane < nrec) w0 = *(const float2 *)(ml + lane * ml_stride);
-    float2 xw = make_float2(NEG_INF, 0.f);
-    if (XR && lane < x_n) xw = *(const float2 *)(x_ml + 2 * lane);
+    if (lane < nall) w0 = *(const float2 *)ml_at(lane);
     // The outputs of the first 8 records go out with the weights (they do not
     // depend on them), so a row of up to 8 records costs one round trip.
-    vecd v0[8], xv[XR ? 8 : 1];
-    if (!XR || nrec > 0) {
+    vecd v0[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v0[j] = *(const vecd *)(o + min(j, nrec - 1) * o_stride + lane * DPL);
-    }
-    if constexpr (XR) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < x_n) xv[j] = *(const vecd *)(x_o + (int64_t)j * D + lane * DPL);
-    }
-    float M = XR ? fmaxf(w0.x, xw.x) : w0.x;
-    for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, ml[k * ml_stride]);
+    for (int j = 0; j < 8; ++j) v0[j] = *(const vecd *)(o_at(min(j, nall - 1)) + lane * DPL);
+    float M = w0.x;
+    for (int k = lane + 64; k < nall; k += 64) M = fmaxf(M, *ml_at(k));
     M = wave_max(M);
     float lsum = 0.f;
     vecd acc = {};
-    for (int c0 = 0; c0 < nrec; c0 += 64) {
+    for (int c0 = 0; c0 < nall; c0 += 64) {
         float2 w = w0;
         if (c0 > 0) {
             w = make_float2(NEG_INF, 0.f);
-            if (c0 + lane < nrec) w = *(const float2 *)(ml + (c0 + lane) * ml_stride);
+            if (c0 + lane < nall) w = *(const float2 *)ml_at(c0 + lane);
         }
-        const float f = (w.x == NEG_INF) ? 0.f : fast_exp2(w.x - M);  // 0 past nrec
+        const float f = (w.x == NEG_INF) ? 0.f : fast_exp2(w.x - M);  // 0 past nall
         lsum = fmaf(f, w.y, lsum);
-        const int n = min(64, nrec - c0);
+        const int n = min(64, nall - c0);
         for (int j0 = 0; j0 < n; j0 += 8) {
             vecd v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int k = c0 + min(j0 + j, n - 1);  // padded slots reload a valid record
-                v[j] = (c0 == 0 && j0 == 0) ? v0[j] : *(const vecd *)(o + k * o_stride + lane * DPL);
+                v[j] = (c0 == 0 && j0 == 0) ? v0[j] : *(const vecd *)(o_at(k) + lane * DPL);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -1573,14 +1576,6 @@ __device__ __forceinline__ void merge_records(T *__restrict__ dst, const float *
                 acc += fj * v[j];
             }
         }
-    }
-    if constexpr (XR) {
-        const float fx = (xw.x == NEG_INF) ? 0.f : fast_exp2(xw.x - M);  // 0 past x_n
-        lsum = fmaf(fx, xw.y, lsum);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < x_n)
-                acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fx), j)) * xv[j];
     }
     lsum = group_sum<16>(lsum);
     lsum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), 0)) +

@@ -409,6 +409,50 @@ pa_status scratch_for_current_device(void **ptr) {
     return PA_OK;
 }
 
+// Shared-prefix decode: the prefix pass runs on a second stream of the
+// library (default priority, one per device, created on first use) beside
+// the suffix pass on the caller's stream.  A prefix workgroup fits on a CU
+// next to a suffix one, so the matrix-core work of the prefix pass hides under
+// the memory-bound suffix pass.  The enqueue sequence (fork event, prefix
+// launch, join event, suffix launch, join wait, reduce) is done under the
+// device's lock, so calls from several host threads interleave safely.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex mu;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init_mu;
+
+pa_status side_for_current_device(SideStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PA_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_side_init_mu);
+    SideStream &sd = g_side[dev];
+    if (!sd.stream) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (j) (void)hipEventDestroy(j);
+            if (f) (void)hipEventDestroy(f);
+            if (st) (void)hipStreamDestroy(st);
+            return fail(PA_ERR_HIP, "side stream for the prefix pass: %s", hipGetErrorString(e));
+        }
+        sd.fork = f;
+        sd.join = j;
+        sd.stream = st;
+    }
+    *out = &sd;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -680,13 +724,24 @@ pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_
         if (s != PA_OK) return s;
         return hip_status(pa::launch_decode_reduce(st.a, (hipStream_t)stream), "decode_reduce");
     }
-    s = hip_status(pa::launch_decode_prefix(st.a, px, (hipStream_t)stream), "decode_prefix");
+    SideStream *sd = nullptr;
+    s = side_for_current_device(&sd);
     if (s != PA_OK) return s;
-    s = hip_status(pa::launch_decode_suffix(st.a, plan.prefix_tokens, (hipStream_t)stream),
-                   "decode_suffix");
+    std::lock_guard<std::mutex> lock(sd->mu);
+    const hipStream_t caller = (hipStream_t)stream;
+    s = hip_status(hipEventRecord(sd->fork, caller), "hipEventRecord");
+    if (s == PA_OK) s = hip_status(hipStreamWaitEvent(sd->stream, sd->fork, 0), "hipStreamWaitEvent");
+    if (s == PA_OK)
+        s = hip_status(pa::launch_decode_prefix(st.a, px, sd->stream), "decode_prefix");
+    if (s == PA_OK) s = hip_status(hipEventRecord(sd->join, sd->stream), "hipEventRecord");
     if (s != PA_OK) return s;
-    return hip_status(pa::launch_decode_reduce_prefix(st.a, px, (hipStream_t)stream),
-                      "decode_reduce");
+    s = hip_status(pa::launch_decode_suffix(st.a, plan.prefix_tokens, caller), "decode_suffix");
+    // The caller's stream waits for the prefix pass whatever happened above,
+    // so that nothing later on it can overtake work already enqueued.
+    const pa_status w = hip_status(hipStreamWaitEvent(caller, sd->join, 0), "hipStreamWaitEvent");
+    if (s != PA_OK) return s;
+    if (w != PA_OK) return w;
+    return hip_status(pa::launch_decode_reduce_prefix(st.a, px, caller), "decode_reduce");
 }
 
 pa_status pa_decode_append_partitions(void *out, const void *query, const void *new_key,
