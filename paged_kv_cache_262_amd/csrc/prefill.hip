@@ -21,13 +21,22 @@
 //
 // Staging.  Key blocks are gathered through the block table straight from
 // HBM into LDS (global_load_lds_dwordx4: each lane moves 16 bytes, no
-// registers), one pair of blocks ahead of the pair being multiplied, in two
-// LDS stages that alternate; the even-parity waves issue their share of it
-// before their products, the odd-parity ones after their softmax, so the
-// memory pipeline moves it while the matrix cores work.  K and V rows keep their memory layout
-// [key][dim]; the 16-byte chunks of each row are permuted by an XOR with a
-// function of the key so that the matrix-operand reads below hit distinct
-// LDS banks.  The block-table entries of the tile sit in an LDS window.
+// registers) in two LDS stages that alternate.  K and V rows keep their
+// memory layout [key][dim]; the 16-byte chunks of each row are permuted by an
+// XOR with a function of the key so that the matrix-operand reads below hit
+// distinct LDS banks.  For whole blocks the page address of each 1 KB DMA
+// segment is wave-uniform and computed on the scalar unit.
+//
+// Schedule (bf16).  Each wave runs a two-deep software pipeline over its
+// blocks: in step t it computes S^T of its block of pair t, then issues the
+// P V products of its block of pair t - 1 one at a time, each with a slice of
+// the vector work of the softmax of pair t (row maxima, exponentials, bf16
+// packing), so the matrix cores and the vector ALUs work at the same time.
+// V is therefore staged one step after K: the stage read in step t holds K of
+// pair t and V of pair t - 1, and the DMA issued in step t fills the other
+// stage with K of pair t + 1 and V of pair t (the V movers at once, the K
+// movers after their S^T products, which keeps the two waves of a SIMD
+// balanced).
 //
 // Products.  They are computed transposed, S^T = K Q^T and O^T = V^T P^T.
 // The K operand (16 keys x 32 dims) is one 16-byte LDS read per lane; the
@@ -37,6 +46,8 @@
 // operands), so P never goes through LDS; and the V^T operand (16 dims x 8
 // keys per lane) comes from row-major V through the transposing LDS read
 // ds_read_b64_tr_b16, 4 keys of one dim per read.
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 #include "pa_prefill_append.h"
@@ -51,19 +62,12 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef PA_PF_WAVES
-#define PA_PF_WAVES 8
-#endif
-constexpr int kPfWaves = PA_PF_WAVES;  // waves per workgroup: 2 key parities x row groups
+constexpr int kPfWaves = 8;  // waves per workgroup: 2 key parities x 4 row groups
 constexpr int kPfRows = 128;        // rows (query x head) per workgroup
 constexpr int kKeyBlock = 64;       // keys per LDS block
 constexpr int kXcds = 8;            // MI355X: 8 accelerator complex dies, one L2 each
 constexpr float kPfRescale = 8.0f;  // log2 units
 constexpr int kBtCache = 2048;      // block-table entries a tile keeps in LDS
-#ifndef PA_PF_HALVES
-#define PA_PF_HALVES 2
-#endif
-constexpr int kPfHalves = PA_PF_HALVES;  // 32-key halves of a block per softmax pass (1 or 2)
 
 template <typename A, typename Bv>
 __device__ __forceinline__ floatx4_v mfma16x16x32(const A &a, const Bv &b, floatx4_v c) {
@@ -78,15 +82,48 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));  // RNE
 }
 
+// Maxima written as the instructions themselves: fmaxf makes the compiler
+// quiet each operand that it cannot prove canonical (every MFMA result)
+// with an extra v_max first, which doubles the vector work of the row
+// maxima.  A NaN operand is ignored, as by fmaxf; a NaN logit makes its
+// weight NaN whatever the maximum is.
+__device__ __forceinline__ float vmax2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Maximum of the 4 NKT logits a lane holds for row tile rt of s[NKT][RT]:
+// two values per instruction, in two independent chains.
+template <int NKT, int RT>
+__device__ __forceinline__ float lane_max(const floatx4_v (&s)[NKT][RT], int rt) {
+    constexpr int N = 4 * NKT;
+    float a = s[0][rt][0], b = s[0][rt][1];
+    int i = 2;
+#pragma unroll
+    for (; i + 4 <= N; i += 4) {
+        a = vmax3(a, s[i / 4][rt][i % 4], s[(i + 1) / 4][rt][(i + 1) % 4]);
+        b = vmax3(b, s[(i + 2) / 4][rt][(i + 2) % 4], s[(i + 3) / 4][rt][(i + 3) % 4]);
+    }
+#pragma unroll
+    for (; i + 2 <= N; i += 2) a = vmax3(a, s[i / 4][rt][i % 4], s[(i + 1) / 4][rt][(i + 1) % 4]);
+    return vmax2(a, b);
+}
+
 // Max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes holding
 // one row of an MFMA result), with lane swaps instead of LDS shuffles.
 __device__ __forceinline__ float row_max4(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = vmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
@@ -167,7 +204,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     // operand reads of one stage do not wait for the DMA filling the other.
     __shared__ __attribute__((aligned(1024))) char stage_a[LY::STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char stage_b[LY::STAGE_BYTES];
-    __shared__ int bt_s[kBtCache];
 
     // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
     // L2).  Renumber them so that the tiles of one (chunk, kv head), which
@@ -228,35 +264,27 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     }
 
     const int64_t block_elems = (int64_t)B * D * num_kv_heads;
+    const int64_t block_bytes = block_elems * 2;
+    // Table entries at or past this (negative ones included, as unsigned)
+    // are outside the pool.
+    const uint32_t nb_u32 = (uint32_t)min(num_blocks, (int64_t)1 << 31);
     const int nkb = cdiv(kend, kKeyBlock);
     const int npairs = cdiv(nkb, 2);
-    const int nbt = cdiv(kend, B);  // pages the tile reads
 
-    // ---- block-table window -------------------------------------------------
-    // Entries of pages [win_p0, win_p0 + kBtCache).  It is refilled (rarely:
-    // every 32K keys at 16-token pages) before the DMA of a pair it does not
-    // cover; barriers separate the refill from the reads on both sides.
-    constexpr int kWinBlocks = kBtCache * B / kKeyBlock;
-    static_assert(kWinBlocks % 2 == 0, "windows hold whole pairs");
-    int win_kb0 = 0, win_p0 = 0;
-    auto load_window = [&](int kb0) __attribute__((always_inline)) {
-        win_kb0 = kb0;
-        win_p0 = kb0 * (kKeyBlock / B);
-        const int cnt = min(nbt - win_p0, kBtCache);
-        for (int i = tid; i < cnt; i += kPfWaves * 64) bt_s[i] = bt[win_p0 + i];
-    };
-
-    // ---- DMA of one pair of key blocks into a stage -------------------------
-    // The stage's 4 * SEGS segments of 1 KB ([K even][K odd][V even][V odd])
-    // are split over the waves; lane i of a segment moves chunk i % NCH of row
-    // i / NCH.  The rows of a segment lie in one page, so each segment is one
-    // global_load_lds from a wave-uniform page address plus a per-lane offset
-    // that depends only on the segment's parity.  In the tile's last block,
-    // keys past kend read the row of key kend - 1 instead (data whose weight
-    // is exactly 0), so no LDS row is ever left stale.
+    // ---- DMA of one tensor's share of a pair into a stage -------------------
+    // A stage holds four 64-key blocks, [K even][K odd][V even][V odd], as
+    // 4 * SEGS segments of 1 KB split over the waves: the first half of the
+    // waves moves K segments, the other half V segments.  Lane i of a segment
+    // moves chunk i % NCH of row i / NCH.  The rows of a segment lie in one
+    // page.  For a block wholly inside the tile's keys the page is
+    // wave-uniform: its table entry is a scalar load and its address scalar
+    // arithmetic, so the vector ALUs, which the softmax needs, do none of this
+    // work; the lanes add only their offset inside the segment (which depends
+    // only on the segment's parity).  In the tile's last block, keys past kend
+    // read the row of key kend - 1 instead (data whose weight is exactly 0),
+    // so no LDS row is ever left stale.
     const int seg_row = lane / LY::NCH, seg_ch = lane % LY::NCH;
     static_assert(B % LY::KPS == 0, "a segment's rows share a page");
-    static_assert(LY::SEGS_PER_WAVE <= 64, "one lane per segment");
     static_assert(LY::swz(2 * LY::KPS) == LY::swz(0) && LY::swz(3 * LY::KPS) == LY::swz(LY::KPS),
                   "the chunk permutation of a segment depends on its parity only");
     uint32_t seg_lane_off[2];
@@ -264,56 +292,48 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     for (int par = 0; par < 2; ++par)
         seg_lane_off[par] = (uint32_t)(seg_row * ROWB +
                                        ((seg_ch ^ LY::swz(par * LY::KPS + seg_row)) << 4));
-    // Lane j < SEGS_PER_WAVE computes the global address of the first row of
-    // the wave's segment j of pair pr (its page looked up in the window,
-    // out-of-range entries replaced by block 0), all segments in one pass.
-    auto lookup_pages = [&](int pr) __attribute__((always_inline)) -> uint64_t {
-        const int j = lane < LY::SEGS_PER_WAVE ? lane : 0;
-        const int seg = w * LY::SEGS_PER_WAVE + j;
-        const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1;
+    constexpr int SPW = LY::SEGS_PER_WAVE;
+    static_assert(LY::SEGS % SPW == 0, "a wave's segments lie in one block");
+    const int dma_tensor = (w * SPW) / (2 * LY::SEGS);  // 0: K, 1: V (uniform)
+    auto issue_dma = [&](char *stage, int pr) __attribute__((always_inline)) {
+        const int seg0 = w * SPW;
+        const int bp = (seg0 / LY::SEGS) & 1, s0 = seg0 % LY::SEGS;
         const int kb = 2 * pr + bp;
-        const int key_s = min(kb * kKeyBlock + (seg % LY::SEGS) * LY::KPS, kend - 1);
-        int phys = bt_s[key_s / B - win_p0];
-        if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;  // caller error: block 0
-        const char *pool = (const char *)(tensor ? value_cache : key_cache);
-        return (uint64_t)(uintptr_t)(pool + ((int64_t)phys * block_elems + (int64_t)g * B * D) * 2 +
-                                     (key_s % B) * ROWB);
-    };
-    // This wave's share of the DMA of pair pr into stage (seg_addr from
-    // lookup_pages(pr)).
-    auto issue_dma = [&](char *stage, int pr, uint64_t seg_addr) __attribute__((always_inline)) {
+        if (kb >= nkb) return;  // block past the tile's keys
+        char *dst0 = stage + (dma_tensor * 2 + bp) * LY::BLOCK_BYTES + s0 * 1024;
+        const char *pool = (const char *)(dma_tensor ? value_cache : key_cache);
+        if (kb * kKeyBlock + kKeyBlock <= (AP ? min(kend, new0) : kend)) {
+            const char *head = pool + (int64_t)g * B * D * 2;
 #pragma unroll
-        for (int j = 0; j < LY::SEGS_PER_WAVE; ++j) {
-            const int seg = w * LY::SEGS_PER_WAVE + j;  // uniform
-            const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1;
-            const int s = seg % LY::SEGS;
-            const int kb = 2 * pr + bp;
-            if (kb >= nkb) continue;  // block past the tile's keys
-            lds_void *dst = (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024);
-            if (kb * kKeyBlock + kKeyBlock <= (AP ? min(kend, new0) : kend)) {
-                const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)seg_addr, j);
-                const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(seg_addr >> 32), j);
-                const char *page = (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-                __builtin_amdgcn_global_load_lds((const void *)(page + seg_lane_off[s & 1]), dst, 16,
-                                                 0, 0);
-            } else {
-                const int kk = s * LY::KPS + seg_row;
-                const int key = min(kb * kKeyBlock + kk, kend - 1);
-                const char *src;
-                if (AP && key >= new0) {  // one of the chunk's own rows
-                    const bf16_t *rows = tensor ? new_value : new_key;
-                    src = (const char *)(rows + ((int64_t)(q_begin + key - new0) * num_kv_heads +
-                                                 g) * D) +
-                          ((seg_ch ^ LY::swz(kk)) << 4);
-                } else {
-                    int phys = bt_s[key / B - win_p0];
-                    if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;
-                    const char *pool = (const char *)(tensor ? value_cache : key_cache);
-                    src = pool + ((int64_t)phys * block_elems + ((int64_t)g * B + key % B) * D) * 2 +
-                          ((seg_ch ^ LY::swz(kk)) << 4);
-                }
-                __builtin_amdgcn_global_load_lds((const void *)src, dst, 16, 0, 0);
+            for (int j = 0; j < SPW; ++j) {
+                const int sg = s0 + j;
+                const int key_s = kb * kKeyBlock + sg * LY::KPS;
+                uint32_t phys = (uint32_t)bt[key_s / B];
+                if (phys >= nb_u32) phys = 0;  // caller error: block 0
+                const char *page = head + (int64_t)phys * block_bytes + (key_s % B) * ROWB;
+                __builtin_amdgcn_global_load_lds((const void *)(page + seg_lane_off[sg & 1]),
+                                                 (lds_void *)(dst0 + j * 1024), 16, 0, 0);
             }
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const int sg = s0 + j;
+            const int kk = sg * LY::KPS + seg_row;
+            const int key = min(kb * kKeyBlock + kk, kend - 1);
+            const char *src;
+            if (AP && key >= new0) {  // one of the chunk's own rows
+                const bf16_t *rows = dma_tensor ? new_value : new_key;
+                src = (const char *)(rows + ((int64_t)(q_begin + key - new0) * num_kv_heads + g) * D) +
+                      ((seg_ch ^ LY::swz(kk)) << 4);
+            } else {
+                uint32_t phys = (uint32_t)bt[key / B];
+                if (phys >= nb_u32) phys = 0;
+                src = pool + (int64_t)phys * block_bytes + (((int64_t)g * B + key % B) * D) * 2 +
+                      ((seg_ch ^ LY::swz(kk)) << 4);
+            }
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(dst0 + j * 1024), 16,
+                                             0, 0);
         }
     };
 
@@ -330,168 +350,228 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
     const uint32_t v_lane_off = v_row * ROWB + (l16 & 1) * 8 +
                                 ((LY::swz(v_row) ^ ((l16 & 3) >> 1)) << 4);
 
-    // One 64-key block of this wave's parity: S^T = K Q^T, online softmax,
-    // O^T += V^T P^T, in 64 / (32 NH) passes of NH 32-key halves (fewer
-    // passes: fewer rescale checks; more: a smaller live S / P^T state).
-    // dma_stage != nullptr: issue this wave's share of the DMA of pair
-    // dma_pair after the first pass's softmax, before its P V products.
-    constexpr int NH = kPfHalves;     // 32-key halves per pass
-    constexpr int NKT = 2 * NH;       // 16-key tiles per pass
-    constexpr int VB = 4 / NH;        // dim tiles per batch of transposing reads
-    static_assert(DT % VB == 0, "dim tiles split into batches");
-    auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
-                       uint64_t seg_phys) __attribute__((always_inline)) {
-        const uint32_t vbase = lds_addr(Vb) + v_lane_off;
+    // ---- the three parts of a block -------------------------------------------
+    // S^T = K Q^T for the 64 keys of block Kb: s[kt][rt] holds keys
+    // kt * 16 + 4 * lg + i (element i) of row (rg * RT + rt) * 16 + l16.
+    constexpr int NKT = kKeyBlock / 16;
+    auto qk = [&](const char *Kb, floatx4_v (&s)[NKT][RT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int hp = 0; hp < 2 / NH; ++hp) {
-            const int kt0 = hp * NKT;  // first 16-key tile of the pass
-            floatx4_v s[NKT][RT];
-            __builtin_amdgcn_s_setprio(0);  // products at the base priority
+        for (int kt = 0; kt < NKT; ++kt) {
+            u32x4 kf[KS];
 #pragma unroll
-            for (int kt = 0; kt < NKT; ++kt) {
-                u32x4 kf[KS];
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kf[ks] = *(const u32x4 *)(Kb + (kt0 + kt) * 16 * ROWB + k_row_off +
-                                              (((ks * 4 + lg) ^ k_sw) << 4));
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    floatx4_v a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kf[ks], qf[rt][ks], a);
-                    s[kt][rt] = a;
-                }
-            }
-            // The softmax runs at a raised priority: the SIMD's other wave
-            // keeps the matrix core busy meanwhile, and this wave's vector
-            // work is not held back behind it.
-            __builtin_amdgcn_s_setprio(1);
-            // Causal mask: only passes that reach past the tile's first
-            // position need it (a uniform branch).  Masked logits are -inf,
-            // never scaled.
-            const int pkey0 = key0 + kt0 * 16;
-            if (pkey0 + NKT * 16 - 1 > pos0) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (pkey0 + kt * 16 + lg * 4 + i > row_pos[rt]) s[kt][rt][i] = NEG_INF;
-            }
-            u32x4 pf[RT][NH];  // P^T operands: [rt][32-key half of the pass]
+            for (int ks = 0; ks < KS; ++ks)
+                kf[ks] = *(const u32x4 *)(Kb + kt * 16 * ROWB + k_row_off +
+                                          (((ks * 4 + lg) ^ k_sw) << 4));
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                float mx = NEG_INF;
+                floatx4_v a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-                    mx = fmaxf(mx, fmaxf(fmaxf(s[kt][rt][0], s[kt][rt][1]),
-                                         fmaxf(s[kt][rt][2], s[kt][rt][3])));
-                mx = row_max4(mx);
-                // The reference maximum m_row (log2 units) is raised only
-                // when a logit exceeds it by more than kPfRescale, so the
-                // rescale of the accumulators is rare; weights stay below
-                // 2^kPfRescale.
-                const float cand = mx * scale_log2;
-                if (__builtin_amdgcn_ballot_w64(cand > m_row[rt] + kPfRescale)) {
-                    const float mn = fmaxf(m_row[rt], cand);
-                    const float alpha = (m_row[rt] == NEG_INF) ? 0.f : fast_exp2(m_row[rt] - mn);
-                    m_row[rt] = mn;
-                    acc_l[rt] *= alpha;
+                for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kf[ks], qf[rt][ks], a);
+                s[kt][rt] = a;
+            }
+        }
+    };
+    // Causal mask: only blocks that reach past the tile's first position need
+    // it (a uniform branch).  Masked logits are -inf, never scaled.
+    auto mask_s = [&](floatx4_v (&s)[NKT][RT], int key0) __attribute__((always_inline)) {
+        if (key0 + kKeyBlock - 1 > pos0) {
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] *= alpha;
-                }
-                const float mneg = (m_row[rt] == NEG_INF) ? 0.f : -m_row[rt];
-                float p[NKT][4];
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        p[kt][i] = fast_exp2(fmaf(s[kt][rt][i], scale_log2, mneg));
+                        if (key0 + kt * 16 + lg * 4 + i > row_pos[rt]) s[kt][rt][i] = NEG_INF;
+        }
+    };
+    // Reference maximum of row tile rt (log2 units) from its block maximum x.
+    // m_row is raised only when a logit exceeds it by more than kPfRescale, so
+    // rescales are rare and weights stay below 2^kPfRescale.  alpha brings the
+    // accumulators to the new reference; the caller applies it after the
+    // products still pending on the old one.  Returns whether alpha may differ
+    // from 1 (wave-uniform).
+    float mneg[RT];  // -m_row, or 0 while m_row is -inf
+    auto new_reference = [&](int rt, float x, float &alpha) __attribute__((always_inline)) -> bool {
+        const float cand = x * scale_log2;
+        const bool need = __builtin_amdgcn_ballot_w64(cand > m_row[rt] + kPfRescale) != 0;
+        const float mn = need ? fmaxf(m_row[rt], cand) : m_row[rt];
+        alpha = (!need || m_row[rt] == NEG_INF) ? (need ? 0.f : 1.f) : fast_exp2(m_row[rt] - mn);
+        m_row[rt] = mn;
+        mneg[rt] = (mn == NEG_INF) ? 0.f : -mn;
+        return need;
+    };
+    // Weight of logit e (row tile e / 16, key tile (e / 4) % 4, element
+    // e % 4), kept in s; after every second one the pair is packed into the
+    // P^T operand (keys of half kt / 2, word (kt % 2) * 2 + i / 2).
+    auto weight = [&](floatx4_v (&s)[NKT][RT], u32x4 (&pn)[RT][2], int e)
+                      __attribute__((always_inline)) {
+        const int rt = e / 16, kt = (e / 4) % 4, i = e % 4;
+        s[kt][rt][i] = fast_exp2(fmaf(s[kt][rt][i], scale_log2, mneg[rt]));
+        if (i & 1)
+            pn[rt][kt / 2][(kt % 2) * 2 + i / 2] = pack_bf16x2(s[kt][rt][i - 1], s[kt][rt][i]);
+    };
+    // Transposing reads of V^T for batch b (dim tiles 2b, 2b + 1) of the block
+    // at Vb, through the compiler builtin: the address derives from the stage,
+    // so no wait for the DMA into the other stage is added.
+    typedef s16x4 VBatch[2][2][2];  // [dim tile of the batch][key half][rows +0 / +16]
+    auto read_v = [&](const char *Vb, VBatch &dst, int b) __attribute__((always_inline)) {
 #pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    pf[rt][h][0] = pack_bf16x2(p[2 * h][0], p[2 * h][1]);
-                    pf[rt][h][1] = pack_bf16x2(p[2 * h][2], p[2 * h][3]);
-                    pf[rt][h][2] = pack_bf16x2(p[2 * h + 1][0], p[2 * h + 1][1]);
-                    pf[rt][h][3] = pack_bf16x2(p[2 * h + 1][2], p[2 * h + 1][3]);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+                    dst[j][h][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4 *)(Vb + (v_lane_off ^ ((uint32_t)(2 * b + j) << 5)) +
+                                      (2 * h + r) * 16 * ROWB));
+    };
+    // Product q (0..7) of batch b: O^T of dim tile 2b + q / 4 += V^T P^T over
+    // key half (q / 2) % 2, row tile q % 2.
+    auto pv_product = [&](const VBatch &v, const u32x4 (&pp)[RT][2], int b, int q)
+                          __attribute__((always_inline)) {
+        const int j = q / 4, h = (q / 2) % 2, rt = q % 2;
+        const s16x8 vf = __builtin_shufflevector(v[j][h][0], v[j][h][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[2 * b + j][rt] = mfma16x16x32(vf, pp[rt][h], acc_o[2 * b + j][rt]);
+    };
+    static_assert(RT == 2 && DT % 2 == 0, "two row tiles, dim tiles in pairs");
+    constexpr int NB = DT / 2;  // batches of V^T reads
+    // The block's second half: O^T += V^T P^T and the row sums (a ones row
+    // against the same bf16 P^T the output uses, so numerator and denominator
+    // agree) for the weights pp of the previous block, whose V is at Vb (PV),
+    // and the softmax of this block's logits s into the weights pn (SM).
+    // With both, each matrix product is issued with a slice of the softmax's
+    // vector work, and full scheduling barriers keep that order, so the
+    // products run on the matrix cores while the maxima and exponentials run
+    // on the vector ALUs.  Returns whether the accumulators need the factors
+    // alpha (after the products).
+    auto pv_softmax = [&](const char *Vb, const u32x4 (&pp)[RT][2], floatx4_v (&s)[NKT][RT],
+                          u32x4 (&pn)[RT][2], float (&alpha)[RT], auto pv_tag, auto sm_tag)
+                          __attribute__((always_inline)) -> bool {
+        constexpr bool PV = decltype(pv_tag)::value, SM = decltype(sm_tag)::value;
+        bool any = false;
+        if constexpr (!PV) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) any |= new_reference(rt, row_max4(lane_max(s, rt)), alpha[rt]);
+#pragma unroll
+            for (int e = 0; e < 16 * RT; ++e) weight(s, pn, e);
+            return any;
+        } else {
+            VBatch vb[2];
+            read_v(Vb, vb[0], 0);
+            if constexpr (!SM) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        acc_l[rt] = mfma16x16x32(ones_row, pp[rt][h], acc_l[rt]);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if (b + 1 < NB) read_v(Vb, vb[(b + 1) & 1], b + 1);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) pv_product(vb[b & 1], pp, b, q);
                 }
-                // Row sums on the matrix core: a ones row against the same
-                // bf16 P^T the output uses, so numerator and denominator agree.
+                return false;
+            } else {
+                // Row sums and the first batch, with the block maxima.
+                float lm[RT], x[RT];
 #pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
-            }
-            if (hp == 0 && dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
-            // O^T += V^T P^T over the pass's halves, VB dim tiles per batch;
-            // the transposing reads of the next batch are in flight while the
-            // current one multiplies.
-            s16x4 vb[2][VB][NH][2];  // [buffer][dim tile of the batch][half][rows +0 / +16]
-            auto issue_v = [&](s16x4 (&dst)[VB][NH][2], int dt0) __attribute__((always_inline)) {
+                for (int rt = 0; rt < RT; ++rt) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc_l[rt] = mfma16x16x32(ones_row, pp[rt][0], acc_l[rt]);
+                    acc_l[rt] = mfma16x16x32(ones_row, pp[rt][1], acc_l[rt]);
+                    lm[rt] = lane_max(s, rt);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                read_v(Vb, vb[1], 1);
 #pragma unroll
-                for (int j = 0; j < VB; ++j) {
-                    const uint32_t a = (vbase + (uint32_t)(hp * NH * 32 * ROWB)) ^
-                                       ((uint32_t)(dt0 + j) << 5);
-                    dst[j][0][0] = lds_read_tr16(a);
-                    dst[j][0][1] = lds_read_tr16_off<16 * ROWB>(a);
-                    if constexpr (NH == 2) {
-                        dst[j][NH - 1][0] = lds_read_tr16_off<32 * ROWB>(a);
-                        dst[j][NH - 1][1] = lds_read_tr16_off<48 * ROWB>(a);
+                for (int q = 0; q < 8; q += 2) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    pv_product(vb[0], pp, 0, q);
+                    pv_product(vb[0], pp, 0, q + 1);
+                    if (q < 2 * RT) {
+                        if (q / 2 < RT) x[q / 2] = row_max4(lm[q / 2]);
+                    } else {
+                        const int rt = q / 2 - RT;
+                        any |= new_reference(rt, x[rt], alpha[rt]);
                     }
                 }
-            };
-            issue_v(vb[0], 0);
-            __builtin_amdgcn_s_setprio(0);
+                // The other batches, each product with one or two weights.
 #pragma unroll
-            for (int b = 0; b < DT / VB; ++b) {
-                lds_wait(vb[b & 1]);
-                if (b + 1 < DT / VB) issue_v(vb[(b + 1) & 1], VB * (b + 1));
+                for (int b = 1; b < NB; ++b) {
 #pragma unroll
-                for (int j = 0; j < VB; ++j)
+                    for (int q = 0; q < 8; ++q) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (q == 0 && b + 1 < NB) read_v(Vb, vb[(b + 1) & 1], b + 1);
+                        pv_product(vb[b & 1], pp, b, q);
+                        const int m = (b - 1) * 8 + q, nm = (NB - 1) * 8;
 #pragma unroll
-                    for (int h = 0; h < NH; ++h) {
-                        const s16x8 vf = __builtin_shufflevector(vb[b & 1][j][h][0],
-                                                                 vb[b & 1][j][h][1], 0, 1, 2, 3,
-                                                                 4, 5, 6, 7);
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-                            acc_o[VB * b + j][rt] =
-                                mfma16x16x32(vf, pf[rt][h], acc_o[VB * b + j][rt]);
+                        for (int e = m * 16 * RT / nm; e < (m + 1) * 16 * RT / nm; ++e)
+                            weight(s, pn, e);
                     }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                return any;
             }
-            __builtin_amdgcn_s_setprio(1);
         }
     };
 
-    // One pair: wait for its stage, start the next pair's DMA into the other
-    // stage, multiply this wave's block of the pair.  The two waves of a SIMD
-    // have different parities: the even one issues its share of the DMA at
-    // once, the odd one after its softmax, so the memory pipeline drains one
-    // share while the other wave multiplies.
-    auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
+    // ---- main loop -------------------------------------------------------------
+    // Step t: S^T of this wave's block of pair t (its K in the current stage),
+    // then the P V products of its block of pair t - 1 (that V is in the
+    // current stage too) on the matrix cores while the weights of pair t are
+    // computed on the vector ALUs.  The DMA issued during step t fills the
+    // other stage with K of pair t + 1 and V of pair t, so two stages suffice.
+    u32x4 pf[RT][2];  // weights of this wave's block of the previous pair
+    auto step = [&](char *cur, char *nxt, int t) __attribute__((always_inline)) {
         __syncthreads();  // cur's DMA landed (every wave waited for its own); nxt is free
-        const bool next = pr + 1 < npairs;
-        uint64_t seg_phys = 0;
-        if (next) {
-            if (2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
-                load_window(2 * (pr + 1));
-                __syncthreads();
+        const bool has_s = t < npairs && 2 * t + kp < nkb;
+        const bool has_pv = t >= 1 && 2 * (t - 1) + kp < nkb;
+        const int dpair = dma_tensor ? t : t + 1;
+        const bool dma = dpair < npairs;
+        // The V movers (odd parity) issue their share at once, the K movers
+        // (even parity) after their S^T products; a wave with no S^T to
+        // compute issues it at once.
+        const bool late = dma && has_s && kp == 0;
+        if (dma && !late) issue_dma(nxt, dpair);
+        const char *Kb = cur + kp * LY::BLOCK_BYTES;
+        const char *Vb = cur + (2 + kp) * LY::BLOCK_BYTES;
+        using yes = std::true_type;
+        using no = std::false_type;
+        if (has_s) {
+            floatx4_v s[NKT][RT];
+            qk(Kb, s);
+            if (late) issue_dma(nxt, dpair);
+            __builtin_amdgcn_sched_barrier(0);
+            mask_s(s, (2 * t + kp) * kKeyBlock);
+            __builtin_amdgcn_sched_barrier(0);
+            float alpha[RT];
+            u32x4 pn[RT][2];
+            const bool rescale = has_pv ? pv_softmax(Vb, pf, s, pn, alpha, yes{}, yes{})
+                                        : pv_softmax(Vb, pf, s, pn, alpha, no{}, yes{});
+            if (rescale) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    acc_l[rt] *= alpha[rt];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) acc_o[dt][rt] *= alpha[rt];
+                }
             }
-            seg_phys = lookup_pages(pr + 1);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) pf[rt][h] = pn[rt][h];
+        } else if (has_pv) {
+            floatx4_v s[NKT][RT];
+            u32x4 pn[RT][2];
+            float alpha[RT];
+            pv_softmax(Vb, pf, s, pn, alpha, yes{}, no{});
         }
-        const bool works = 2 * pr + kp < nkb;
-        const bool late = next && works && kp == 1;
-        if (next && !late) issue_dma(nxt, pr + 1, seg_phys);
-        if (works)
-            compute(cur + kp * LY::BLOCK_BYTES, cur + (2 + kp) * LY::BLOCK_BYTES,
-                    (2 * pr + kp) * kKeyBlock, late ? nxt : nullptr, pr + 1, seg_phys);
     };
 
-    load_window(0);
-    __syncthreads();
-    if (npairs > 0) issue_dma(stage_a, 0, lookup_pages(0));
-    for (int pr = 0; pr < npairs; pr += 2) {
-        step(stage_a, stage_b, pr);
-        if (pr + 1 < npairs) step(stage_b, stage_a, pr + 1);
+    if (npairs > 0 && dma_tensor == 0) issue_dma(stage_a, 0);
+    for (int t = 0; t <= npairs; t += 2) {
+        step(stage_a, stage_b, t);
+        if (t + 1 <= npairs) step(stage_b, stage_a, t + 1);
     }
     if (AP) {
         // The K and V rows of this tile's queries (kv head g) into their
@@ -737,20 +817,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
     for (int par = 0; par < 2; ++par)
         seg_lane_off[par] = (uint32_t)(seg_row * D + ((seg_ch ^ LY::swz(par * LY::KPS + seg_row)) << 4));
     const char *kpool = (const char *)key_cache, *vpool = (const char *)value_cache;
-    auto lookup_pages = [&](int pr) __attribute__((always_inline)) -> uint64_t {
-        const int j = lane < LY::SEGS_PER_WAVE ? lane : 0;
-        const int seg = w * LY::SEGS_PER_WAVE + j;
-        const int tensor = seg / (2 * LY::SEGS), bp = (seg / LY::SEGS) & 1, s = seg % LY::SEGS;
-        const int kb = 2 * pr + bp;
-        if (tensor == 0) {
-            const int key_s = min(kb * kKeyBlock + s * LY::KPS, kend - 1);
-            return (uint64_t)(uintptr_t)(kpool + page_of(key_s) + (key_s % B) * D);
-        }
-        const int pg = s / LY::SEGS_PER_PAGE;
-        const int key_p = min(kb * kKeyBlock + pg * B, kend - 1);
-        return (uint64_t)(uintptr_t)(vpool + page_of(key_p) + (s % LY::SEGS_PER_PAGE) * 1024);
+    // Offset of the page holding key `key` (a wave-uniform key: the table
+    // entry is a scalar load and the offset scalar arithmetic).
+    auto page_of_uniform = [&](int key) __attribute__((always_inline)) -> int64_t {
+        int phys = bt[key / B];
+        if (phys < 0 || (int64_t)phys >= num_blocks) phys = 0;  // caller error: block 0
+        return ((int64_t)phys * num_kv_heads + g) * page_stride;
     };
-    auto issue_dma = [&](char *stage, int pr, uint64_t seg_addr) __attribute__((always_inline)) {
+    auto issue_dma = [&](char *stage, int pr) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < LY::SEGS_PER_WAVE; ++j) {
             const int seg = w * LY::SEGS_PER_WAVE + j;  // uniform
@@ -759,12 +833,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
             const int kb = 2 * pr + bp;
             if (kb >= nkb) continue;
             lds_void *dst = (lds_void *)(stage + (tensor * 2 + bp) * LY::BLOCK_BYTES + s * 1024);
-            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)seg_addr, j);
-            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(seg_addr >> 32), j);
-            const char *base = (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
             if (tensor == 1) {
+                const int key_p = min(kb * kKeyBlock + (s / LY::SEGS_PER_PAGE) * B, kend - 1);
+                const char *base =
+                    vpool + page_of_uniform(key_p) + (s % LY::SEGS_PER_PAGE) * 1024;
                 __builtin_amdgcn_global_load_lds((const void *)(base + lane * 16), dst, 16, 0, 0);
             } else if (kb * kKeyBlock + kKeyBlock <= kend) {
+                const int key_s = kb * kKeyBlock + s * LY::KPS;
+                const char *base = kpool + page_of_uniform(key_s) + (key_s % B) * D;
                 __builtin_amdgcn_global_load_lds((const void *)(base + seg_lane_off[s & 1]), dst, 16,
                                                  0, 0);
             } else {
@@ -778,8 +854,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
     };
 
     // One 64-key block of this wave's parity.
-    auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair,
-                       uint64_t seg_phys) __attribute__((always_inline)) {
+    auto compute = [&](const char *Kb, const char *Vb, int key0, char *dma_stage, int dma_pair)
+                       __attribute__((always_inline)) {
         floatx4_v s[4][RT];
         __builtin_amdgcn_s_setprio(0);  // products at the base priority, softmax raised
 #pragma unroll
@@ -816,12 +892,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
         u32x4 pf[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float mx = NEG_INF;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-                mx = fmaxf(mx, fmaxf(fmaxf(s[kt][rt][0], s[kt][rt][1]),
-                                     fmaxf(s[kt][rt][2], s[kt][rt][3])));
-            mx = row_max4(mx);
+            const float mx = row_max4(lane_max(s, rt));
             const float cand = mx * scale_log2;
             if (__builtin_amdgcn_ballot_w64(cand > m_row[rt] + kPfRescale)) {
                 const float mn = fmaxf(m_row[rt], cand);
@@ -847,7 +918,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h) acc_l[rt] = mfma16x16x32(ones_row, pf[rt][h], acc_l[rt]);
         }
-        if (dma_stage != nullptr) issue_dma(dma_stage, dma_pair, seg_phys);
+        if (dma_stage != nullptr) issue_dma(dma_stage, dma_pair);
         __builtin_amdgcn_s_setprio(0);
         // O^T += V^T P^T: dim dt * 16 + l16, keys 32 h + 8 lg + [0, 8).
         const bool tail = key0 + kKeyBlock > kend;
@@ -878,25 +949,21 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_fp8_kernel(
     auto step = [&](char *cur, char *nxt, int pr) __attribute__((always_inline)) {
         __syncthreads();
         const bool next = pr + 1 < npairs;
-        uint64_t seg_phys = 0;
-        if (next) {
-            if (2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
-                load_window(2 * (pr + 1));
-                __syncthreads();
-            }
-            seg_phys = lookup_pages(pr + 1);
+        if (next && 2 * (pr + 1) + 2 > win_kb0 + kWinBlocks) {
+            load_window(2 * (pr + 1));
+            __syncthreads();
         }
         const bool works = 2 * pr + kp < nkb;
         const bool late = next && works && kp == 1;
-        if (next && !late) issue_dma(nxt, pr + 1, seg_phys);
+        if (next && !late) issue_dma(nxt, pr + 1);
         if (works)
             compute(cur + kp * LY::BLOCK_BYTES, cur + (2 + kp) * LY::BLOCK_BYTES,
-                    (2 * pr + kp) * kKeyBlock, late ? nxt : nullptr, pr + 1, seg_phys);
+                    (2 * pr + kp) * kKeyBlock, late ? nxt : nullptr, pr + 1);
     };
 
     load_window(0);
     __syncthreads();
-    if (npairs > 0) issue_dma(stage_a, 0, lookup_pages(0));
+    if (npairs > 0) issue_dma(stage_a, 0);
     for (int pr = 0; pr < npairs; pr += 2) {
         step(stage_a, stage_b, pr);
         if (pr + 1 < npairs) step(stage_b, stage_a, pr + 1);
