@@ -307,6 +307,25 @@ def test_fp8_prefill_empty_long_and_many_chunks():
     check_close(out, ref, "bf16", "fp8 prefill edge chunks")
 
 
+@pytest.mark.parametrize("B", [16, 32])
+def test_fp8_prefill_context_beyond_the_table_window(B):
+    """A chunk over a 40,000-token context in FP8 pools (seeded random codes):
+    at 16-token blocks its tiles read 2,500 pages, more than the 2,048
+    block-table entries the FP8 prefill keeps in LDS, so the kernel refills
+    that window mid-way (at 32-token blocks it does not: the control case)."""
+    c = W.make_case("pf8_long", 191 + B, "bf16", 8, 2, 128, B, [3], new_positions=[2],
+                    chunks=[(64, 40000)], extra_blocks=2)
+    NB = c.key_cache.shape[0]
+    kc8 = W.random_fp8_codes(411 + B, (NB, 2, B, 128))
+    vc8 = W.random_fp8_codes(412 + B, (NB, 2, 128, B))
+    ks, vs = 1.0 / 16, 1.0 / 8
+    say("fp8 prefill long context", B)
+    out = gpu_prefill_fp8(c, kc8, vc8, ks, vs)
+    ref = oracle.prefill_fp8(c.chunk_query, kc8, vc8, c.chunk_block_tables, c.chunk_cu_query_lens,
+                             c.chunk_context_lens, c.scale, ks, vs)
+    check_close(out, ref, "bf16", f"fp8 prefill 40K context B{B}")
+
+
 def test_fp8_prefill_mixed_workload():
     """The mixed chunked-prefill shape (2 chunks of 512 queries over 2,048 prior
     tokens, 32 q / 8 kv heads, d 128, B 16): the chunks' own tokens are written

@@ -155,10 +155,9 @@ def test_prefill_last_row_matches_decode():
 
 @pytest.mark.parametrize("B", [16, 32])
 def test_prefill_context_beyond_the_table_window(B):
-    """A chunk over a 40,000-token context: at 16-token blocks its tiles read
-    2,500 pages, more than the 2,048 block-table entries a tile keeps in LDS,
-    so the kernel refills that window mid-way (at 32-token blocks it does not:
-    the control case)."""
+    """A chunk over a 40,000-token context (2,500 pages at 16-token blocks,
+    1,250 at 32): the DMA reads every table entry the tiles reach, far past
+    the first two thousand."""
     c = W.make_case("pf_long", 91 + B, "bf16", 8, 2, 128, B, [3], new_positions=[2],
                     chunks=[(64, 40000)], extra_blocks=2)
     kc, vc = dev(c.key_cache), dev(c.value_cache)
