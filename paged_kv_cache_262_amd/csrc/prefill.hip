@@ -488,12 +488,10 @@ __global__ __launch_bounds__(kPfWaves * 64) void prefill_chunk_kernel(
                     __builtin_amdgcn_sched_barrier(0);
                     pv_product(vb[0], pp, 0, q);
                     pv_product(vb[0], pp, 0, q + 1);
-                    if (q < 2 * RT) {
-                        if (q / 2 < RT) x[q / 2] = row_max4(lm[q / 2]);
-                    } else {
-                        const int rt = q / 2 - RT;
-                        any |= new_reference(rt, x[rt], alpha[rt]);
-                    }
+                    if (q < 2 * RT)
+                        x[q / 2] = row_max4(lm[q / 2]);  // products 0-3: lane swaps
+                    else  // products 4-7: the new reference maxima
+                        any |= new_reference(q / 2 - RT, x[q / 2 - RT], alpha[q / 2 - RT]);
                 }
                 // The other batches, each product with one or two weights.
 #pragma unroll
