@@ -526,7 +526,9 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
     t_pf = avg_ms("pf0", "pf1") if chunks else None
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    wl = case.name + ("_fp8" if fp8 else "")
+    # Key of the profile rows (kernel traces, HBM bytes) for this measurement:
+    # the step with the writes inside the passes runs other kernel variants.
+    wl = case.name + ("_fp8" if fp8 else "") + ("_fused" if mixed_fused else "")
     # bf16 uses the matrix-core variant of the balanced split.
     dp_kernel = ("decode_stream_fp8_kernel" if fp8 else
                  "decode_partition_kernel" if P != 0 or S > 8192 else
