@@ -522,7 +522,10 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
 
     t_cw = avg_ms("cw0", "cw1") if T and not fused and not mixed_fused else None
     t_dp = avg_ms("dp0", "dp1")
-    t_dr = avg_ms("dp1", "dr1") if not sp else None  # inside the one call
+    # The reduce call launches nothing when the decode gives each (sequence,
+    # kv head) pair one wave (small batches of short contexts).
+    has_reduce = binding.decode_needs_reduce(S, Hq, Hkv, D, B, maxL, P)
+    t_dr = avg_ms("dp1", "dr1") if not sp and has_reduce else None  # sp: inside the one call
     t_pf = avg_ms("pf0", "pf1") if chunks else None
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
@@ -580,7 +583,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         "separate_cache_write_ms_per_step": _r(separate_ms),
         "kernels_ms": {"reshape_and_cache": "fused" if (fused or mixed_fused) else _r(t_cw),
                        ("decode_shared_prefix" if sp else "decode_partition"): _r(t_dp),
-                       "decode_reduce": _r(t_dr),
+                       "decode_reduce": _r(t_dr) if (sp or has_reduce) else "none",
                        "prefill_chunk": _r(t_pf)},
         "roofline": roofline(dp_kernel, wl, "hbm", dp_bytes, t_dp, HBM_PEAK_GBS,
                              medians["dp0dp1"]),

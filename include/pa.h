@@ -247,7 +247,12 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
  * pa_decode_partitions writes the final output of every sequence that fits in
  * one partition and the per-partition partial results of the others into the
  * workspace; pa_decode_reduce merges those partials (log-sum-exp rescaling)
- * into out and writes zeros for empty contexts.
+ * into out and writes zeros for empty contexts.  For a small batch of short
+ * contexts (partition_size 0, at most 1,024 (sequence, kv head) pairs and
+ * max_context_len <= 128) the first phase gives each pair one wave, writes
+ * every output row itself (zeros for empty contexts), and pa_decode_reduce
+ * returns PA_OK without launching anything; pa_decode_needs_reduce tells the
+ * two cases apart.
  */
 pa_status pa_decode_partitions(void *out, const void *query, const void *key_cache,
                                const void *value_cache, const int32_t *block_tables,
@@ -263,6 +268,16 @@ pa_status pa_decode_reduce(void *out, const int32_t *context_lens, int32_t num_s
                            int32_t block_size, int32_t max_blocks_per_seq,
                            int32_t max_context_len, int32_t partition_size, int32_t dtype,
                            const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * 1 if pa_decode_reduce launches work for these sizes (the same arguments as
+ * pa_decode_partitions), 0 if pa_decode_partitions finishes every row by
+ * itself (the one-wave-per-pair case above, or an empty batch).  Invalid
+ * sizes give 1.  A host-side query: no device access.
+ */
+int32_t pa_decode_needs_reduce(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                               int32_t partition_size);
 
 /*
  * pa_decode_append -- one decode step with its new tokens: the cache write of

@@ -33,6 +33,7 @@ SIGNATURES = {
                                     _vp]),
     "pa_decode_auto_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_needs_reduce": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _i32, _i32, _f, _i32, _vp, _sz, _vp]),
     "pa_decode_no_alloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -166,6 +167,14 @@ def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_
                            max_context_len, partition_size=0) -> int:
     return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                 block_size, max_context_len, partition_size))
+
+
+def decode_needs_reduce(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, partition_size=0) -> bool:
+    """Whether pa_decode_reduce launches work for these sizes (False: the first
+    phase finishes every row, one wave per (sequence, kv head) pair)."""
+    return bool(load().pa_decode_needs_reduce(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, max_context_len, partition_size))
 
 
 def auto_partition_size(num_seqs, num_kv_heads, max_context_len, block_size) -> int:

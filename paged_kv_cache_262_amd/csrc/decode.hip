@@ -350,6 +350,39 @@ __device__ __forceinline__ int wave_of_unit(int64_t u, int64_t U, int nw) {
 // Exclusive scan of the per-sequence unit counts into scan[0..S], by a
 // workgroup of NW waves.  scan[S] is the total per kv head.  Sequence s counts
 // context_lens[s] - len_skip tokens (its tokens past the first len_skip).
+// The unit range [ua, ub) of wave gw: an equal share of the batch's U units
+// over nw waves (the balanced split), or with nw == 0 the units of pair gw
+// (one wave per sequence and kv head; the range is empty for an empty pair).
+// False: the wave has nothing to do.
+__device__ __forceinline__ bool wave_range(const int *scan, int S, int Hkv, int64_t U, int nw,
+                                           int gw, int64_t &ua, int64_t &ub) {
+    if (nw == 0) {
+        if (gw >= S * Hkv) return false;
+        const int s = gw / Hkv, g = gw - s * Hkv;
+        const int us = scan[s + 1] - scan[s];
+        ua = (int64_t)scan[s] * Hkv + (int64_t)g * us;
+        ub = ua + us;
+        return true;
+    }
+    // With fewer units than waves only the first U waves work, so that every
+    // working wave owns at least one unit (the reduce relies on it).
+    const int nwe = (int)min((int64_t)nw, U);
+    if (gw >= nwe) return false;
+    ua = U * gw / nwe;
+    ub = U * (gw + 1) / nwe;
+    return true;
+}
+
+// One wave per pair: the G output rows of an empty pair (a sequence of
+// length 0) are zero, as the reduce writes them in the balanced split.
+template <typename T, int D>
+__device__ __forceinline__ void zero_pair_rows(T *out, int gw, int Hkv, int num_q_heads, int G,
+                                               int lane) {
+    const int s = gw / Hkv, g = gw - s * Hkv;
+    T *dst = out + ((int64_t)s * num_q_heads + (int64_t)g * G) * D;
+    for (int i = lane; i < G * D; i += 64) Elem<T>::store(dst + i, 0.f);
+}
+
 template <int NW>
 __device__ void scan_units(int *scan, const int32_t *__restrict__ context_lens, int S,
                            int max_tokens, int len_skip = 0) {
@@ -416,12 +449,13 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
 
     const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
     const int tg = lane / LPT, r = lane % LPT;
-    // With fewer units than waves only the first U waves work, so that every
-    // working wave owns at least one unit (the reduce relies on it).
-    const int nwe = (int)min((int64_t)nw, U);
     const int gw = blockIdx.x * NW + w;
-    if (gw >= nwe) return;
-    const int64_t ua = U * gw / nwe, ub = U * (gw + 1) / nwe;
+    int64_t ua, ub;
+    if (!wave_range(scan, S, Hkv, U, nw, gw, ua, ub)) return;
+    if (ua == ub) {  // one wave per pair, and this pair is empty
+        zero_pair_rows<T, D>(out, gw, Hkv, num_q_heads, G, lane);
+        return;
+    }
 
     const int64_t head_bytes = (int64_t)B * ROWB;
     const int64_t block_bytes = head_bytes * Hkv;
@@ -705,10 +739,13 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
 
     const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int nwe = (int)min((int64_t)nw, U);
     const int gw = blockIdx.x * NW + w;
-    if (gw >= nwe) return;
-    const int64_t ua = U * gw / nwe, ub = U * (gw + 1) / nwe;
+    int64_t ua, ub;
+    if (!wave_range(scan, S, Hkv, U, nw, gw, ua, ub)) return;
+    if (ua == ub) {  // one wave per pair, and this pair is empty
+        zero_pair_rows<bf16_t, D>(out, gw, Hkv, num_q_heads, G, lane);
+        return;
+    }
 
     const int64_t head_bytes = (int64_t)B * ROWB;
     const int64_t block_bytes = head_bytes * Hkv;
@@ -1243,10 +1280,13 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
 
     const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
     const int l16 = lane & 15, lg = lane >> 4;
-    const int nwe = (int)min((int64_t)nw, U);
     const int gw = blockIdx.x * NW + w;
-    if (gw >= nwe) return;
-    const int64_t ua = U * gw / nwe, ub = U * (gw + 1) / nwe;
+    int64_t ua, ub;
+    if (!wave_range(scan, S, Hkv, U, nw, gw, ua, ub)) return;
+    if (ua == ub) {  // one wave per pair, and this pair is empty
+        zero_pair_rows<bf16_t, D>(out, gw, Hkv, num_q_heads, G, lane);
+        return;
+    }
 
     const int64_t head_bytes = (int64_t)B * D;
     const int64_t block_bytes = head_bytes * Hkv;
@@ -1787,6 +1827,10 @@ static int max_tokens(const DecodeArgs &a) {
     return (int)m;
 }
 
+// The balanced-split kernels' wave count argument: the equal split over
+// stream_waves waves, or 0 for one wave per (sequence, kv head) pair.
+static int kernel_waves(const DecodeArgs &a) { return a.pairs ? 0 : a.stream_waves; }
+
 #ifndef PA_DECODE_MMA
 #define PA_DECODE_MMA 1
 #endif
@@ -1802,7 +1846,7 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream, int
                            (const bf16_t *)a.query, (bf16_t *)a.key_cache, (bf16_t *)a.value_cache,
                            a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads,
                            a.num_kv_heads, a.max_blocks_per_seq, max_tokens(a), a.num_blocks,
-                           a.stream_waves, a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
+                           kernel_waves(a), a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
                            (const bf16_t *)a.new_key, (const bf16_t *)a.new_value, len_skip,
                            force_records);
     else
@@ -1811,7 +1855,7 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream, int
                            (const bf16_t *)a.query, (bf16_t *)a.key_cache, (bf16_t *)a.value_cache,
                            a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads,
                            a.num_kv_heads, a.max_blocks_per_seq, max_tokens(a), a.num_blocks,
-                           a.stream_waves, a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
+                           kernel_waves(a), a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan,
                            (const bf16_t *)nullptr, (const bf16_t *)nullptr, len_skip,
                            force_records);
     return hipGetLastError();
@@ -1824,7 +1868,7 @@ static void launch_stream_fp8_as(const DecodeArgs &a, hipStream_t stream) {
                        (size_t)(a.num_seqs + 1) * sizeof(int), stream, (bf16_t *)a.out,
                        (const bf16_t *)a.query, (uint8_t *)a.key_cache, (uint8_t *)a.value_cache,
                        a.block_tables, a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
-                       a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                       a.max_blocks_per_seq, max_tokens(a), a.num_blocks, kernel_waves(a),
                        a.scale * kLog2e * a.k_scale, a.v_scale, a.ws_o, a.ws_ml, a.ws_scan,
                        (const bf16_t *)a.new_key, (const bf16_t *)a.new_value, 1.0f / a.k_scale,
                        1.0f / a.v_scale);
@@ -1855,7 +1899,7 @@ static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
                                dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
                                (T *)a.key_cache, (T *)a.value_cache, a.block_tables,
                                a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
-                               a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                               a.max_blocks_per_seq, max_tokens(a), a.num_blocks, kernel_waves(a),
                                a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan, (const T *)a.new_key,
                                (const T *)a.new_value);
         else
@@ -1863,7 +1907,7 @@ static hipError_t launch_part(const DecodeArgs &a, hipStream_t stream) {
                                dim3(kDecodeWaves * 64), 0, stream, (T *)a.out, (const T *)a.query,
                                (T *)a.key_cache, (T *)a.value_cache, a.block_tables,
                                a.context_lens, a.num_seqs, a.num_q_heads, a.num_kv_heads,
-                               a.max_blocks_per_seq, max_tokens(a), a.num_blocks, a.stream_waves,
+                               a.max_blocks_per_seq, max_tokens(a), a.num_blocks, kernel_waves(a),
                                a.scale * kLog2e, a.ws_o, a.ws_ml, a.ws_scan, (const T *)nullptr,
                                (const T *)nullptr);
     } else {
@@ -1949,6 +1993,7 @@ static hipError_t launch_red(const DecodeArgs &a, hipStream_t stream,
 
 hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
+    if (a.stream_waves > 0 && a.pairs) return hipSuccess;  // every pair finished by its wave
     if (a.dtype == 1)
         return a.head_dim == 64 ? launch_red<bf16_t, 64>(a, stream)
                                 : launch_red<bf16_t, 128>(a, stream);

@@ -76,8 +76,16 @@ int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_
 
 // Decode work split: balanced over waves (partition_size 0, batches up to
 // kStreamMaxSeqs) or fixed partitions.
+// Balanced split: one wave per (sequence, kv head) pair instead of the equal
+// split when the pairs fit in one round of waves and no context is longer than
+// this many 16-token units, so that a small batch of short contexts is one
+// launch (the equal split would cut every pair into single units and need the
+// reduce).
+constexpr int64_t kPairModeUnits = 8;
+
 struct DecodePlan {
     bool stream;
+    bool pairs;      // balanced split with one wave per pair
     int waves;       // balanced split
     int32_t P;       // fixed partitions
     int64_t np;
@@ -87,13 +95,19 @@ struct DecodePlan {
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t block_size, int32_t max_context_len,
-                       int32_t partition_size) {
+                       int32_t partition_size, bool allow_pairs = true) {
     DecodePlan p{};
     const int64_t S = num_seqs > 0 ? num_seqs : 0;
     p.stream = partition_size == 0 && S <= pa::kStreamMaxSeqs;
     if (p.stream) {
-        const int64_t units = S * num_kv_heads * cdiv64(max_context_len > 0 ? max_context_len : 0, 16);
-        p.waves = (int)(units < pa::kStreamWaves ? (units > 0 ? units : 1) : pa::kStreamWaves);
+        const int64_t per_pair = cdiv64(max_context_len > 0 ? max_context_len : 0, 16);
+        const int64_t npairs = S * num_kv_heads;
+        const int64_t units = npairs * per_pair;
+        p.pairs = allow_pairs && npairs > 0 && npairs <= pa::kStreamWaves &&
+                  per_pair <= kPairModeUnits;
+        p.waves = p.pairs ? (int)npairs
+                          : (int)(units < pa::kStreamWaves ? (units > 0 ? units : 1)
+                                                           : pa::kStreamWaves);
         const int64_t G = num_q_heads / num_kv_heads;
         const int64_t recs = (S * num_kv_heads + p.waves) * G;
         p.o_bytes = align256((size_t)recs * head_dim * 4);
@@ -122,7 +136,7 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t max_context_len,
                        int32_t partition_size, float scale, int32_t dtype, void *workspace,
-                       size_t workspace_bytes, bool needs_inputs) {
+                       size_t workspace_bytes, bool needs_inputs, bool allow_pairs = true) {
     pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, dtype);
     if (s != PA_OK) return s;
     if (num_seqs < 0 || num_seqs > 65535)
@@ -150,7 +164,7 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
         }
     }
     const DecodePlan plan = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                        block_size, max_context_len, partition_size);
+                                        block_size, max_context_len, partition_size, allow_pairs);
     const size_t need = plan.total() > kMinWorkspace ? plan.total() : kMinWorkspace;
     const bool uses_ws = num_seqs > 0 && (plan.stream || plan.np > 1);
     if (uses_ws) {
@@ -179,6 +193,7 @@ pa_status setup_decode(DecodeSetup &st, void *out, const void *query, const void
     a.partition_size = plan.stream ? 0 : plan.P;
     a.num_partitions = plan.stream ? 0 : (int)plan.np;
     a.stream_waves = plan.stream ? plan.waves : 0;
+    a.pairs = plan.stream && plan.pairs;
     a.scale = scale;
     a.dtype = dtype;
     a.new_key = nullptr;
@@ -528,6 +543,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return p.total() > kMinWorkspace ? p.total() : kMinWorkspace;
 }
 
+int32_t pa_decode_needs_reduce(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                               int32_t partition_size) {
+    if (num_seqs <= 0) return num_seqs == 0 ? 0 : 1;
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_q_heads % num_kv_heads || partition_size < 0 || max_context_len < 0)
+        return 1;
+    const DecodePlan p = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, partition_size);
+    if (p.stream) return p.pairs ? 0 : 1;
+    return 1;
+}
+
 pa_status pa_decode_partitions(void *out, const void *query, const void *key_cache,
                                const void *value_cache, const int32_t *block_tables,
                                const int32_t *context_lens, int32_t num_seqs,
@@ -636,8 +664,10 @@ PrefixPlan plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
     PrefixPlan p{};
     p.prefix_tokens = prefix_blocks * block_size;
     p.suffix_max_len = max_context_len > p.prefix_tokens ? max_context_len - p.prefix_tokens : 0;
+    // The suffix pass writes every pair as records for the merge with the
+    // prefix records: the equal split, never one wave per pair.
     p.suffix = plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                           p.suffix_max_len, 0);
+                           p.suffix_max_len, 0, false);
     p.ksplit = (num_seqs > 0 && p.prefix_tokens > 0)
                    ? pa::prefix_splits(num_seqs, num_q_heads, num_kv_heads, p.prefix_tokens)
                    : 0;
@@ -704,7 +734,7 @@ pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_
                      block_tables ? block_tables + prefix_blocks : nullptr, context_lens,
                      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                      max_blocks_per_seq, num_blocks, plan.suffix_max_len, 0, scale, PA_BF16,
-                     workspace, workspace_bytes, true);
+                     workspace, workspace_bytes, true, false);
     if (s != PA_OK) return s;
     if (num_seqs == 0) return PA_OK;
     if (debug_checks() &&

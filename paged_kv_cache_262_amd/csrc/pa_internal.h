@@ -56,6 +56,11 @@ struct DecodeArgs {
     int64_t num_blocks;
     int max_context_len, partition_size, num_partitions;
     int stream_waves;  // > 0: balanced split over this many waves; 0: fixed partitions
+    // Nonzero (with stream_waves == S * Hkv): one wave per (sequence, kv head)
+    // pair instead of the equal split, so every pair is finished by its own
+    // wave and no reduce runs.  Chosen for small batches of short contexts,
+    // where the equal split would cut every pair into single units.
+    int pairs;
     float scale;
     int dtype;  // 0 f32, 1 bf16
     // Workspace.  Fixed partitions: ws_o [S][Hq][num_partitions][D] and ws_ml

@@ -62,6 +62,22 @@ def test_auto_partition_and_workspace(lib):
     assert lib.pa_decode_workspace_bytes(4, 4, 4, 64, 16, 100, 128) == 256
 
 
+def test_decode_needs_reduce(lib):
+    """One wave per (sequence, kv head) pair, so no second launch, for at most
+    1,024 pairs with no context above 8 units of 16 tokens; the equal split
+    and the fixed partitions always reduce."""
+    f = lib.pa_decode_needs_reduce
+    assert f(4, 4, 4, 64, 16, 100, 0) == 0
+    assert f(64, 32, 8, 128, 16, 4096, 0) == 1        # 8B decode batch
+    assert f(0, 32, 8, 128, 16, 4096, 0) == 0         # nothing to do
+    assert f(4, 4, 4, 64, 16, 100, 128) == 1          # fixed partitions
+    assert f(128, 32, 8, 128, 16, 128, 0) == 0        # 1,024 pairs of 8 units
+    assert f(129, 32, 8, 128, 16, 128, 0) == 1        # 1,032 pairs
+    assert f(128, 32, 8, 128, 16, 129, 0) == 1        # 9 units
+    assert f(4, 6, 4, 64, 16, 100, 0) == 1            # invalid sizes
+    assert f(-1, 4, 4, 64, 16, 100, 0) == 1
+
+
 def _decode(lib, **kw):
     a = dict(out=A, query=A, kc=A, vc=A, bt=A, lens=A, S=4, Hq=8, Hkv=2, D=128, B=16, mbs=8,
              NB=32, maxL=100, P=0, scale=0.1, dtype=1, ws=A2, wsb=1 << 20, stream=None)
