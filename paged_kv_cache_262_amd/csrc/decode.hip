@@ -141,6 +141,41 @@ struct UnitRegs {
     uint4 v[S::NPASS][S::CPL];
 };
 
+// Cache policy of the buffer loads that stream K and V from the pools (the
+// cache-policy operand of the load builtins; bit 1 is gfx950's nt bit).  A
+// decode launch reads most of the cache once, so those loads are
+// non-temporal: their lines are not kept for reuse in L2 and the last-level
+// cache.  Against the default policy this shortened the 8B decode step from
+// 113.4 to 98.6 us and the 32K one from 187.6 to 170.0 us; K alone or V alone
+// non-temporal gave about a third of that each.  Bytes that other waves read
+// again keep the default policy: blocks shared with a neighbouring sequence
+// (below; the plain decode of 128 sequences over one 1,024-token prefix took
+// 175 us with every load non-temporal, 140 us with this rule), the
+// shared-prefix pass, whose blocks every tile of the batch reads, and the
+// FP8 pages of 32-token blocks, whose 32-byte V rows the two units of a
+// block read half each.  The policy is an immediate of the load, so the
+// kernels split their unit runs where it changes and run one copy of the
+// load pipeline per policy (a branch per load made the compiler wait for
+// each load at the join).
+constexpr int kOnce = 2;   // read once: non-temporal
+constexpr int kReuse = 0;  // read again soon: default policy
+
+// Whether physical block phys, at column col of sequence s's table, is also
+// at that column of the previous or the next sequence's table.  Sequences
+// that share blocks (a common prompt, forked samples) hold them at the same
+// positions of their tables and usually sit next to each other in a batch,
+// so their waves read those blocks again and the loads keep the default
+// policy.  Table entries past a neighbour's length are compared as they are:
+// a false match only changes the cache policy.
+__device__ __forceinline__ bool shared_with_neighbour(const int32_t *__restrict__ block_tables,
+                                                      int S, int max_blocks, int s, int col,
+                                                      int phys) {
+    const int32_t *row = block_tables + (int64_t)s * max_blocks + col;
+    const int prev = s > 0 ? row[-max_blocks] : -1;
+    const int next = s + 1 < S ? row[max_blocks] : -1;
+    return prev == phys || next == phys;
+}
+
 // Buffer resources of one unit in the K and V pools: base = the unit's first
 // byte, range = the unit, or an empty range when there is nothing to read
 // (then every load returns zeros without touching memory).  Loads are thus
@@ -158,7 +193,7 @@ __device__ __forceinline__ UnitRes unit_res(const char *kbase, const char *vbase
                                                      0x00020000)};
 }
 
-template <typename T, int D, int G>
+template <int POL, typename T, int D, int G>
 __device__ __forceinline__ void load_unit(UnitRegs<T, D, G> &R, const UnitRes &res, int lane_off) {
     using S = DecodeShape<T, D, G>;
 #pragma unroll
@@ -167,9 +202,9 @@ __device__ __forceinline__ void load_unit(UnitRegs<T, D, G> &R, const UnitRes &r
         for (int k = 0; k < S::CPL; ++k) {
             const int a = lane_off + pp * S::TPP * S::ROWB + S::LPT * k * 16;
             R.k[pp][k] =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res.k, a, 0, 0));
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res.k, a, 0, POL));
             R.v[pp][k] =
-                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res.v, a, 0, 0));
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res.v, a, 0, POL));
         }
 }
 
@@ -504,7 +539,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
         // Lane k describes unit base + k: its pair, row count and block.
         // With AP, l_new is the row of the unit that holds the new token
         // (its last unit, when the length was not clamped), else -1.
-        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1;
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1, l_keep = 0;
         int l_s = 0, l_j = 0, l_us = 1;
         if (lane < n) {  // from the LDS scan alone
             const int64_t u = base + lane;
@@ -552,6 +587,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
             const int phys = block_tables[(int64_t)l_s * max_blocks + tok / B];
             if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
             l_phys = phys;
+            l_keep = shared_with_neighbour(block_tables, S, max_blocks, l_s, tok / B, phys);
             if (AP && Lraw == L && l_j == l_us - 1 && l_nvalid > 0) l_new = l_nvalid - 1;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
@@ -604,17 +640,18 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
             return unit_res(kbase, vbase, off, nvalid > 0 ? SH::UNIT_BYTES : 0);
         };
 
-        // Segments: runs of units of one (sequence, kv head) pair.  At a pair
-        // boundary the previous pair is finished and the next q is loaded
-        // together with the segment's first NBUF units; inside a segment
-        // NBUF - 1 units stay in flight.
+        // Segments: runs of units of one (sequence, kv head) pair with one
+        // cache policy.  At a pair boundary the previous pair is finished and
+        // the next q is loaded together with the segment's first NBUF units;
+        // inside a segment NBUF - 1 units stay in flight.
         constexpr int NB = SH::NBUF;
         UnitRegs<T, D, G> buf[NB];
         int nv[NB];
         for (int i0 = 0; i0 < n;) {
             const int item = __builtin_amdgcn_readlane(l_item, i0);
-            const uint64_t other =
-                __builtin_amdgcn_ballot_w64(lane < n && lane > i0 && l_item != item);
+            const int keep = __builtin_amdgcn_readlane(l_keep, i0);
+            const uint64_t other = __builtin_amdgcn_ballot_w64(
+                lane < n && lane > i0 && (l_item != item || l_keep != keep));
             const int i1 = other ? (int)__builtin_ctzll(other) : n;  // segment end
             if (item != cur_item) {
                 if (cur_item >= 0) finish();
@@ -625,16 +662,25 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_kernel(
                 acc.load_q((const char *)query +
                                ((int64_t)cur_s * num_q_heads + (int64_t)cur_g * G) * ROWB, r);
             }
+            // One copy of the pipeline per cache policy: the loads of a
+            // segment and the uses of their results stay in one copy.
+            auto run = [&](auto pol) __attribute__((always_inline)) {
+                constexpr int POL = decltype(pol)::value;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                load_unit(buf[b], locate(i0 + b, i1, nv[b]), lane_off);
-            for (int i = i0; i < i1; i += NB) {
+                for (int b = 0; b < NB; ++b)
+                    load_unit<POL>(buf[b], locate(i0 + b, i1, nv[b]), lane_off);
+                for (int i = i0; i < i1; i += NB) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (nv[b] > 0) acc.process(buf[b], nv[b], scale_log2, tg);
-                    load_unit(buf[b], locate(i + NB + b, i1, nv[b]), lane_off);
+                    for (int b = 0; b < NB; ++b) {
+                        if (nv[b] > 0) acc.process(buf[b], nv[b], scale_log2, tg);
+                        load_unit<POL>(buf[b], locate(i + NB + b, i1, nv[b]), lane_off);
+                    }
                 }
-            }
+            };
+            if (keep)
+                run(std::integral_constant<int, kReuse>{});
+            else
+                run(std::integral_constant<int, kOnce>{});
             i0 = i1;
         }
     }
@@ -698,10 +744,11 @@ __device__ __forceinline__ int mma_swz(int row) {
     return D == 128 ? (row & 7) << 1 : ((row >> 1) & 3) << 1;
 }
 
-// 16 bytes per lane from a buffer (offset voff) into LDS at lds + 16 * lane;
-// lanes outside the buffer's range write zeros.
+// 16 bytes per lane from a buffer (offset voff) into LDS at lds + 16 * lane,
+// with cache policy POL; lanes outside the buffer's range write zeros.
+template <int POL>
 __device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_mv *)lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_mv *)lds, 16, voff, 0, 0, POL);
 }
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
@@ -816,7 +863,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
 
     for (int64_t base = ua; base < ub; base += 64) {
         const int n = (int)min((int64_t)64, ub - base);
-        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1;
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1, l_keep = 0;
         int l_s = 0, l_j = 0, l_us = 1;
         if (lane < n) {  // from the LDS scan alone
             const int64_t u = base + lane;
@@ -860,6 +907,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
             const int phys = block_tables[(int64_t)l_s * max_blocks + tok / B];
             if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
             l_phys = phys;
+            l_keep = shared_with_neighbour(block_tables, S, max_blocks, l_s, tok / B, phys);
             if (AP && Lraw == L && l_j == l_us - 1 && l_nvalid > 0) l_new = l_nvalid - 1;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
@@ -902,7 +950,8 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
         // touched and zeros land.
         u32x4 kb[NB][KS];
         int nv[NB];
-        auto issue = [&](int b, int i, int seg_end) __attribute__((always_inline)) {
+        auto issue = [&](auto pol, int b, int i, int seg_end) __attribute__((always_inline)) {
+            constexpr int POL = decltype(pol)::value;
             const int ii = i & 63;
             const int nvalid = (i < seg_end) ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
             const int item = __builtin_amdgcn_readlane(l_item, ii);
@@ -921,13 +970,13 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
 #pragma unroll
             for (int sg = 0; sg < SEGS; ++sg) {
                 const int row = sg * KPS + dma_row;
-                dma16_to_lds(rv, &vslot[w][b][sg * 1024],
-                             row * ROWB + ((dma_ch ^ mma_swz<D>(row)) << 4));
+                dma16_to_lds<POL>(rv, &vslot[w][b][sg * 1024],
+                                  row * ROWB + ((dma_ch ^ mma_swz<D>(row)) << 4));
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kb[b][ks] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + ks * 64, 0, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + ks * 64, 0, POL));
         };
 
         // One unit: logits, online softmax per column, P V.
@@ -971,10 +1020,12 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
                 acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pt, acc_o[dt], 0, 0, 0);
         };
 
+        // Segments: runs of units of one pair with one cache policy.
         for (int i0 = 0; i0 < n;) {
             const int item = __builtin_amdgcn_readlane(l_item, i0);
-            const uint64_t other =
-                __builtin_amdgcn_ballot_w64(lane < n && lane > i0 && l_item != item);
+            const int keep = __builtin_amdgcn_readlane(l_keep, i0);
+            const uint64_t other = __builtin_amdgcn_ballot_w64(
+                lane < n && lane > i0 && (l_item != item || l_keep != keep));
             const int i1 = other ? (int)__builtin_ctzll(other) : n;  // segment end
             if (item != cur_item) {
                 if (cur_item >= 0) finish();
@@ -983,15 +1034,23 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_mma_kernel(
                 cur_g = item - cur_s * Hkv;
                 reset(cur_s, cur_g);
             }
+            // One copy of the pipeline per cache policy: the loads of a
+            // segment and the uses of their results stay in one copy.
+            auto run = [&](auto pol) __attribute__((always_inline)) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) issue(b, i0 + b, i1);
-            for (int i = i0; i < i1; i += NB) {
+                for (int b = 0; b < NB; ++b) issue(pol, b, i0 + b, i1);
+                for (int i = i0; i < i1; i += NB) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (nv[b] > 0) process(b);
-                    issue(b, i + NB + b, i1);
+                    for (int b = 0; b < NB; ++b) {
+                        if (nv[b] > 0) process(b);
+                        issue(pol, b, i + NB + b, i1);
+                    }
                 }
-            }
+            };
+            if (keep)
+                run(std::integral_constant<int, kReuse>{});
+            else
+                run(std::integral_constant<int, kOnce>{});
             i0 = i1;
         }
     }
@@ -1120,13 +1179,13 @@ __global__ __launch_bounds__(NW * 64) void decode_prefix_mma_kernel(
 #pragma unroll
             for (int sg = 0; sg < SEGS; ++sg) {
                 const int row = sg * KPS + dma_row;
-                dma16_to_lds(rv, &vslot[w][b][sg * 1024],
+                dma16_to_lds<kReuse>(rv, &vslot[w][b][sg * 1024],
                              row * ROWB + ((dma_ch ^ mma_swz<D>(row)) << 4));
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kb[b][ks] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + ks * 64, 0, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + ks * 64, 0, kReuse));
         };
 
         auto process = [&](int b) __attribute__((always_inline)) {
@@ -1347,7 +1406,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
 
     for (int64_t base = ua; base < ub; base += 64) {
         const int n = (int)min((int64_t)64, ub - base);
-        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1;
+        int l_item = 0, l_nvalid = 0, l_phys = 0, l_tokoff = 0, l_new = -1, l_keep = 0;
         int l_s = 0, l_j = 0, l_us = 1;
         if (lane < n) {  // from the LDS scan alone
             const int64_t u = base + lane;
@@ -1400,6 +1459,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
             const int phys = block_tables[(int64_t)l_s * max_blocks + tok / B];
             if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
             l_phys = phys;
+            l_keep = shared_with_neighbour(block_tables, S, max_blocks, l_s, tok / B, phys);
             if (AP && Lraw == L && l_j == l_us - 1 && l_nvalid > 0) l_new = l_nvalid - 1;
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
@@ -1443,7 +1503,8 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
         // empty ranges: no memory is touched and zeros land.
         u32x4 kb[NB][KW];
         int nv[NB];
-        auto issue = [&](int b, int i, int seg_end) __attribute__((always_inline)) {
+        auto issue = [&](auto pol, int b, int i, int seg_end) __attribute__((always_inline)) {
+            constexpr int POL = decltype(pol)::value;
             const int ii = i & 63;
             const int nvalid = (i < seg_end) ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
             const int item = __builtin_amdgcn_readlane(l_item, ii);
@@ -1459,13 +1520,18 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
                 0x00020000);
             // V first: waiting for this unit's K registers then also covers
             // its DMA (loads complete in issue order).
+            // A unit of a 32-token block reads half of each 32-byte V row
+            // and the block's other unit the rest, from the caches: there
+            // both tensors keep the default policy (non-temporal K alone made
+            // the FP8 32K decode 4% slower).
+            constexpr int UPOL = B == kUnitTokens ? POL : kReuse;
 #pragma unroll
             for (int sg = 0; sg < VSEG; ++sg)
-                dma16_to_lds(rv, &vslot[w][b][sg * 1024], (sg * 64 + lane) * B);
+                dma16_to_lds<UPOL>(rv, &vslot[w][b][sg * 1024], (sg * 64 + lane) * B);
 #pragma unroll
             for (int c = 0; c < KW; ++c)
                 kb[b][c] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + c * 16, 0, 0));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + c * 16, 0, UPOL));
         };
 
         auto process = [&](int b) __attribute__((always_inline)) {
@@ -1528,10 +1594,12 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
             }
         };
 
+        // Segments: runs of units of one pair with one cache policy.
         for (int i0 = 0; i0 < n;) {
             const int item = __builtin_amdgcn_readlane(l_item, i0);
-            const uint64_t other =
-                __builtin_amdgcn_ballot_w64(lane < n && lane > i0 && l_item != item);
+            const int keep = __builtin_amdgcn_readlane(l_keep, i0);
+            const uint64_t other = __builtin_amdgcn_ballot_w64(
+                lane < n && lane > i0 && (l_item != item || l_keep != keep));
             const int i1 = other ? (int)__builtin_ctzll(other) : n;  // segment end
             if (item != cur_item) {
                 if (cur_item >= 0) finish();
@@ -1540,15 +1608,23 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
                 cur_g = item - cur_s * Hkv;
                 reset(cur_s, cur_g);
             }
+            // One copy of the pipeline per cache policy: the loads of a
+            // segment and the uses of their results stay in one copy.
+            auto run = [&](auto pol) __attribute__((always_inline)) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) issue(b, i0 + b, i1);
-            for (int i = i0; i < i1; i += NB) {
+                for (int b = 0; b < NB; ++b) issue(pol, b, i0 + b, i1);
+                for (int i = i0; i < i1; i += NB) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (nv[b] > 0) process(b);
-                    issue(b, i + NB + b, i1);
+                    for (int b = 0; b < NB; ++b) {
+                        if (nv[b] > 0) process(b);
+                        issue(pol, b, i + NB + b, i1);
+                    }
                 }
-            }
+            };
+            if (keep)
+                run(std::integral_constant<int, kReuse>{});
+            else
+                run(std::integral_constant<int, kOnce>{});
             i0 = i1;
         }
     }
@@ -1732,12 +1808,12 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
     UnitRegs<T, D, G> buf[NB];
     int nv[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) load_unit(buf[b], locate(b, nv[b]), lane_off);
+    for (int b = 0; b < NB; ++b) load_unit<kOnce>(buf[b], locate(b, nv[b]), lane_off);
     for (int i = 0; i < nmine; i += NB) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (nv[b] > 0) acc.process(buf[b], nv[b], scale_log2, tg);
-            load_unit(buf[b], locate(i + NB + b, nv[b]), lane_off);
+            load_unit<kOnce>(buf[b], locate(i + NB + b, nv[b]), lane_off);
         }
     }
 
