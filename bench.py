@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0,
                     help="0: balanced split over waves (default); >0: fixed partitions")
     ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--device-warmup-ms", type=float, default=50.0,
+                    help="before the --warmup steps, run the same steps untimed for this long "
+                         "(wall time), so that the timed steps see the clocks of a device that "
+                         "has been busy; 0 turns it off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="the oracle baseline repeats its full-workload run until this much "
@@ -282,7 +286,7 @@ def main():
         copy_probe(args.copy_probe_mib, dev)
     result, reps = measure(case, dev, fp8, args.partition_size, args.steps, args.warmup,
                            args.replicas, args.streams, not args.no_shared_prefix,
-                           args.fused_writes)
+                           args.fused_writes, args.device_warmup_ms)
     del reps
     torch.cuda.empty_cache()
     ceilings = None
@@ -291,7 +295,7 @@ def main():
         for wname, wfp8, opts, tag in EXTRA_WORKLOADS:
             wcase = case if wname == name else W.NAMED[wname]()
             r, wreps = measure(wcase, dev, wfp8, 0, args.steps, args.warmup, args.replicas,
-                               **opts)
+                               device_warmup_ms=args.device_warmup_ms, **opts)
             del wreps
             torch.cuda.empty_cache()
             result["workloads"][wname + ("_fp8" if wfp8 else "") + tag] = summary(r)
@@ -319,7 +323,7 @@ def copy_probe(mib, dev):
 
 
 def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix=True,
-            fuse_writes=False):
+            fuse_writes=False, device_warmup_ms=50.0):
     """Times `steps` steps of the hot path on one workload (after `warmup`
     untimed ones), then the same steps again with an event around each kernel
     for the per-kernel breakdown.  Returns (result dict, device replicas)."""
@@ -474,19 +478,39 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         return e0.elapsed_time(e1) / n, time.perf_counter() - t0
 
     run_step = overlapped_step if overlap else (lambda i: step(i, False))
+    # The garbage collector is off from here on: a collection that stalls the
+    # host long enough to drain the queue would show up inside one interval.
+    # It runs once before the warm-up, not between warm-up and timing: a host
+    # pause of some milliseconds there lets the GPU clocks drop, and the first
+    # timed steps then ran 2-6% slower than the same steps timed again.
+    gc.collect()
+    gc.disable()
+    # Device warm-up: the same steps, untimed, for device_warmup_ms of wall
+    # time (the host waits for the device every 16 steps, so the time is the
+    # device's).  An idle device raises its clocks over the first tens of
+    # milliseconds of sustained work; measured on this part, the first 200
+    # steps timed after a 20-step warm-up ran 1.5% (8B decode) to 6% (mixed
+    # step) slower than the same steps timed again, and 400 more untimed
+    # steps removed the difference.
+    n_dev = 0
+    t_end = time.perf_counter() + device_warmup_ms / 1e3
+    while time.perf_counter() < t_end:
+        run_step(n_dev)
+        if overlap:
+            step(n_dev, False)
+        n_dev += 1
+        if n_dev % 16 == 0:
+            torch.cuda.synchronize()
     for i in range(warmup):
         run_step(i)
         if overlap:
             step(i, False)
     torch.cuda.synchronize()
-    print(f"warmup done ({warmup} steps)", file=sys.stderr, flush=True)
+    print(f"warmup done ({n_dev} device warm-up steps, then {warmup} steps)", file=sys.stderr,
+          flush=True)
 
     # The timed steps carry no events between kernels; a second pass of the
-    # same steps records one event around each kernel for the breakdown.  The
-    # garbage collector is off meanwhile: a collection that stalls the host
-    # long enough to drain the queue would show up inside one interval.
-    gc.collect()
-    gc.disable()
+    # same steps records one event around each kernel for the breakdown.
     ms_step, wall = timed(run_step, steps)
     print(f"timed {steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)", file=sys.stderr,
           flush=True)
@@ -550,6 +574,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "device_warmup": {"ms": device_warmup_ms, "steps": n_dev},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
