@@ -79,7 +79,8 @@ def parse():
                     help="sequences whose blocks a copy op moves")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="prefix-sharing workload: the plain decode instead of "
-                         "pa_decode_shared_prefix (whose step also reports the plain one)")
+                         "pa_decode_shared_prefix / pa_decode_fp8_shared_prefix (whose step "
+                         "also reports the plain one)")
     ap.add_argument("--fused-writes", action="store_true",
                     help="chunked-prefill workloads (bf16): write the new tokens inside the "
                          "decode pass (pa_decode_append) and the prefill pass "
@@ -337,11 +338,13 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
     reps = [Replica(case, dev, fp8) for _ in range(max(1, replicas))]
     ws = binding.make_workspace(reps[0].q, reps[0].kc, maxL, P)
     stream = torch.cuda.current_stream()
-    # The prefix-sharing batch (bf16): pa_decode_shared_prefix, which reads the
-    # shared blocks once per tile of sequences instead of once per sequence
-    # (its prefix pass runs on a second stream beside the suffix pass).
+    # The prefix-sharing batch: pa_decode_shared_prefix (pa_decode_fp8_shared_prefix
+    # over FP8 pools), which reads the shared blocks once per tile of sequences
+    # instead of once per sequence (its prefix pass runs on a second stream
+    # beside the suffix pass).
     pb = case.shared_blocks.numel() if case.shared_blocks is not None else 0
-    sp = bool(shared_prefix and pb and not fp8 and case.dtype == "bf16" and P == 0)
+    sp = bool(shared_prefix and pb and case.dtype == "bf16" and P == 0)
+    sp_name = "pa_decode_fp8_shared_prefix" if fp8 else "pa_decode_shared_prefix"
     ws_sp = binding.make_shared_prefix_workspace(reps[0].q, reps[0].kc, maxL, pb) if sp else None
 
     # Algorithmic work per step.
@@ -388,7 +391,15 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
             binding.reshape_and_cache(r.nk, r.nv, r.kc, r.vc, r.slots, stream=stream)
         if record:
             ev["dp0"].append(mark("cw1"))
-        if sp:  # prefix pass, suffix pass and reduce in one call
+        if sp and fp8:  # prefix pass, suffix pass and reduce in one call
+            binding.decode_fp8_shared_prefix(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale,
+                                             maxL, pb, FP8_K_SCALE, FP8_V_SCALE,
+                                             workspace=ws_sp, stream=stream)
+            if record:
+                mark("dp1")
+                mark("dr1")
+            return
+        if sp:
             binding.decode_shared_prefix(r.out, r.q, r.kc, r.vc, r.bt, r.lens, case.scale, maxL,
                                          pb, workspace=ws_sp, stream=stream)
             if record:
@@ -566,7 +577,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
         dp_bytes = dec_bytes + acct.cache_write_bytes(S, Hkv, D, eb,
                                                       src_elem_bytes=case.new_key.element_size())
     if sp:  # one call: prefix pass + suffix pass + reduce
-        dp_kernel = "pa_decode_shared_prefix"
+        dp_kernel = sp_name
     result = {
         "metric": METRICS[case.name] + (", FP8 e4m3 KV cache" if fp8 else ""),
         "value": round(value, 2),
@@ -586,7 +597,7 @@ def measure(case, dev, fp8, P, steps, warmup, replicas, streams=1, shared_prefix
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "context_tokens": sum(lens), "new_tokens": T,
             "split": "balanced" if P == 0 else f"partitions of {P} tokens",
-            "decode": ("pa_decode_shared_prefix (prefix pass, suffix pass, reduce)" if sp
+            "decode": (f"{sp_name} (prefix pass, suffix pass, reduce)" if sp
                        else "pa_decode_partitions + pa_decode_reduce"),
             "cache_write": ("decode tokens inside the decode pass (pa_decode_append), chunk "
                             "tokens inside the prefill pass (pa_prefill_chunk_append)"

@@ -522,6 +522,31 @@ pa_status pa_decode_fp8_partitions(void *out, const void *query, const void *key
                                    size_t workspace_bytes, void *stream);
 
 /*
+ * pa_decode_fp8_shared_prefix -- pa_decode_shared_prefix over e4m3 pools:
+ * the prefix blocks shared by every sequence (entries 0 .. prefix_blocks - 1
+ * of every table row) are read once per matrix-core tile of 16 / G
+ * sequences, the tokens past them by the balanced split of pa_decode_fp8,
+ * and the reduce merges both ("Configuring vLLM and PagedAttention for High
+ * Throughput Enterprise LLM Serving", section "Zero-Copy Prefix Caching &
+ * Shared Sampling", with the quantised cache of "vLLM Guide: High-Throughput
+ * Multi-GPU LLM Serving with PagedAttention", the quantisation support among
+ * the engine's pillars).  The result is that of pa_decode_fp8 on the same
+ * arguments up to fp32 rounding order.  Arguments, layouts and errors as
+ * pa_decode_fp8 plus prefix_blocks, workspace and side stream as
+ * pa_decode_shared_prefix; the workspace size is
+ * pa_decode_shared_prefix_workspace_bytes() (the same records).
+ */
+pa_status pa_decode_fp8_shared_prefix(void *out, const void *query, const void *key_cache,
+                                      const void *value_cache, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks,
+                                      int32_t max_context_len, int32_t prefix_blocks, float scale,
+                                      float k_scale, float v_scale, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
  * Block manager (host side) -- the allocator that produces the block tables
  * and slot mappings the kernels above read.
  *

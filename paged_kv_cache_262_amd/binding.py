@@ -72,6 +72,9 @@ SIGNATURES = {
                                     _i32, _i32, _i32, _i64, _f, _f, _f, _vp]),
     "pa_decode_fp8_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                         _i32, _i32, _i64, _i32, _f, _f, _f, _vp, _sz, _vp]),
+    "pa_decode_fp8_shared_prefix": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                           _i32, _i32, _i64, _i32, _i32, _f, _f, _f, _vp, _sz,
+                                           _vp]),
     "pa_bm_create": (_i32, [_i64, _i32, _i32, _vp]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_sequence": (_i32, [_vp, _i64, _vp, _i32, _vp, _vp]),
@@ -395,6 +398,20 @@ def decode_fp8(out, query, key_cache, value_cache, block_tables, context_lens, s
                                                   block_tables, context_lens, max_context_len,
                                                   scale, k_scale, v_scale, workspace),
                                 _stream(stream)))
+    return out
+
+
+def decode_fp8_shared_prefix(out, query, key_cache, value_cache, block_tables, context_lens,
+                             scale, max_context_len, prefix_blocks, k_scale, v_scale,
+                             workspace=None, stream=None):
+    """decode_shared_prefix over FP8 pools; writes bf16 ``out`` [S, Hq, D]."""
+    if workspace is None:
+        workspace = make_shared_prefix_workspace(query, key_cache, max_context_len,
+                                                 prefix_blocks)
+    a = _fp8_decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
+                         max_context_len, scale, k_scale, v_scale, workspace)
+    _check(load().pa_decode_fp8_shared_prefix(*a[:14], int(prefix_blocks), *a[14:],
+                                              _stream(stream)))
     return out
 
 

@@ -1326,14 +1326,15 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
     int num_q_heads, int num_kv_heads, int max_blocks, int max_tokens, int64_t num_blocks, int nw,
     float scale_log2, float v_scale, float *__restrict__ rec_o, float *__restrict__ rec_ml,
     int *__restrict__ ws_scan, const bf16_t *__restrict__ new_key,
-    const bf16_t *__restrict__ new_value, float k_inv, float v_inv) {
+    const bf16_t *__restrict__ new_value, float k_inv, float v_inv, int len_skip,
+    int force_records) {
     constexpr int KS = D / 32, DT = D / 16, KB = D / 4, KW = KB / 16;
     constexpr int NB = kFp8Buffers;
     static_assert(G <= 16, "group fits the 16 columns");
     constexpr int VSEG = D / 64;  // V DMA instructions per unit
     extern __shared__ int scan[];  // [S + 1], sized at launch
     __shared__ __attribute__((aligned(1024))) char vslot[NW][NB][D * 16];
-    scan_units<NW>(scan, context_lens, S, max_tokens);
+    scan_units<NW>(scan, context_lens, S, max_tokens, len_skip);
     const int Hkv = num_kv_heads;
     const int64_t U = (int64_t)scan[S] * Hkv;
     if (blockIdx.x == 0)
@@ -1382,7 +1383,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
     auto finish = [&]() __attribute__((always_inline)) {
         const int us = scan[cur_s + 1] - scan[cur_s];
         const int64_t u0 = (int64_t)scan[cur_s] * Hkv + (int64_t)cur_g * us;
-        const bool whole = u0 >= ua && u0 + us <= ub;
+        const bool whole = !force_records && u0 >= ua && u0 + us <= ub;
         const float lsum = __shfl(acc_l[0], l16);
         if (l16 >= G) return;
         const int64_t qrow = (int64_t)cur_s * num_q_heads + (int64_t)cur_g * G + l16;
@@ -1453,7 +1454,7 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
             first_row = fetch_row(first);
         }
         if (lane < n) {
-            const int Lraw = context_lens[l_s];
+            const int Lraw = past_skip(context_lens[l_s], len_skip);
             const int L = clamp_len(Lraw, max_tokens);
             const int tok = l_j * kUnitTokens;
             l_nvalid = min(kUnitTokens, L - tok);
@@ -1631,6 +1632,194 @@ __global__ __launch_bounds__(NW * 64) void decode_stream_fp8_kernel(
         }
     }
     if (cur_item >= 0) finish();
+}
+
+// ---------------------------------------------------------------------------
+// Shared prefix over an FP8 cache: the work split, columns and records of
+// decode_prefix_mma_kernel (16 / G sequences x the G query heads of one kv
+// head per wave, a 1 / ksplit share of the prefix's units, one record per
+// column), with the loads, code widening and V path of
+// decode_stream_fp8_kernel (K codes into registers and widened to bf16 for
+// the S^T product; V pages by DMA into a slot and read back as 4-byte words
+// of 4 tokens).  Records hold v_scale * o, as the FP8 balanced split's do,
+// so the reduce merges both kinds unchanged.  Every prefix unit is whole
+// (the prefix is whole blocks); column c's keys stop at min(L_s, P) through
+// its logits, and the codes past that are written cache entries of the
+// shared blocks.
+// ---------------------------------------------------------------------------
+template <int D, int B, int G, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_prefix_fp8_kernel(
+    const bf16_t *__restrict__ query, const uint8_t *__restrict__ key_cache,
+    const uint8_t *__restrict__ value_cache, const int32_t *__restrict__ prefix_table,
+    const int32_t *__restrict__ context_lens, int S, int num_q_heads, int num_kv_heads,
+    int64_t num_blocks, int prefix_tokens, int ksplit, float scale_log2, float v_scale,
+    float *__restrict__ x_o, float *__restrict__ x_ml) {
+    constexpr int KS = D / 32, DT = D / 16, KB = D / 4, KW = KB / 16;
+    constexpr int NB = kPrefixBuffers;
+    constexpr int VSEG = D / 64;  // V DMA instructions per unit
+    constexpr int CPW = 16 / G;   // sequences per wave
+    __shared__ __attribute__((aligned(1024))) char vslot[NW][NB][D * 16];
+
+    const int lane = threadIdx.x & 63, w = uniform(threadIdx.x >> 6);
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int Hkv = num_kv_heads;
+    const int ncg = cdiv(S, CPW);
+    // Consecutive wave numbers share a kv head, so its prefix pages: keep
+    // them on one XCD (workgroups are dispatched round-robin over the XCDs).
+    const int total = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid % kXcds, idx = bid / kXcds;
+    const int q8 = total / kXcds, rem = total % kXcds;
+    const int lin = xcd < rem ? xcd * (q8 + 1) + idx : rem * (q8 + 1) + (xcd - rem) * q8 + idx;
+    const int gw = lin * NW + w;
+    const int k = gw % ksplit, rest = gw / ksplit;
+    const int cg = rest % ncg, g = rest / ncg;
+    if (g >= Hkv) return;
+
+    const int s = cg * CPW + l16 / G, hh = l16 % G;  // this lane's column
+    const bool col_ok = s < S;
+    int lim = 0;
+    if (col_ok) {
+        const int L = context_lens[s];
+        lim = L < 0 ? 0 : min(L, prefix_tokens);
+    }
+    const int nu = cdiv(prefix_tokens, kUnitTokens);
+    const int u0 = (int)((int64_t)nu * k / ksplit), u1 = (int)((int64_t)nu * (k + 1) / ksplit);
+
+    const int64_t head_bytes = (int64_t)B * D;
+    const int64_t block_bytes = head_bytes * Hkv;
+    const char *kbase = (const char *)key_cache;
+    const char *vbase = (const char *)value_cache;
+    const int k_off = l16 * D + lg * KB;  // from the unit's first K row
+    const uint32_t v_lane = (uint32_t)(l16 * 16 + lg * 4);
+    const s16x4_mv ones_a = l16 == 0 ? s16x4_mv{0x3F80, 0x3F80, 0x3F80, 0x3F80} : s16x4_mv{0, 0, 0, 0};
+
+    u32x4 qt[KS];
+    {
+        const char *qrow = (const char *)query +
+                           ((int64_t)(col_ok ? s : 0) * num_q_heads + (int64_t)g * G + hh) * (D * 2);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = *(const u32x4 *)(qrow + (lg * KB + 8 * ks) * 2);
+            qt[ks] = col_ok ? v : u32x4{0, 0, 0, 0};
+        }
+    }
+    f32x4_mv acc_o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x4_mv{0.f, 0.f, 0.f, 0.f};
+    f32x4_mv acc_l = {0.f, 0.f, 0.f, 0.f};
+    float m_col = NEG_INF;
+
+    for (int c0 = u0; c0 < u1; c0 += 64) {
+        const int n = min(64, u1 - c0);
+        // Lane j: unit c0 + j of the prefix (its page from row 0 of the table).
+        int l_nvalid = 0, l_phys = 0, l_tokoff = 0;
+        if (lane < n) {
+            const int tok = (c0 + lane) * kUnitTokens;
+            l_nvalid = min(kUnitTokens, prefix_tokens - tok);
+            l_tokoff = tok % B;
+            const int phys = prefix_table[tok / B];
+            if (phys < 0 || (int64_t)phys >= num_blocks) l_nvalid = 0;  // caller error
+            l_phys = phys;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the descriptors above: vmcnt(0)
+
+        u32x4 kb[NB][KW];
+        int nv[NB], ut[NB];
+        auto issue = [&](int b, int i) __attribute__((always_inline)) {
+            const int ii = i & 63;
+            const int nvalid = i < n ? __builtin_amdgcn_readlane(l_nvalid, ii) : 0;
+            const int phys = __builtin_amdgcn_readlane(l_phys, ii);
+            const int tokoff = __builtin_amdgcn_readlane(l_tokoff, ii);
+            const int64_t page =
+                nvalid > 0 ? (int64_t)phys * block_bytes + (int64_t)g * head_bytes : 0;
+            nv[b] = nvalid;
+            ut[b] = (c0 + i) * kUnitTokens;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(kbase + page + (int64_t)tokoff * D), (short)0, nvalid > 0 ? nvalid * D : 0,
+                0x00020000);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(vbase + page + tokoff), (short)0,
+                nvalid > 0 ? (D - 1) * B + kUnitTokens : 0, 0x00020000);
+#pragma unroll
+            for (int sg = 0; sg < VSEG; ++sg)
+                dma16_to_lds<kReuse>(rv, &vslot[w][b][sg * 1024], (sg * 64 + lane) * B);
+#pragma unroll
+            for (int c = 0; c < KW; ++c)
+                kb[b][c] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + c * 16, 0, kReuse));
+        };
+
+        auto process = [&](int b) __attribute__((always_inline)) {
+            // The NB - 1 younger units issued VSEG + KW loads each: once they
+            // are the only ones left, this unit's K and V have arrived.
+            asm volatile("s_waitcnt vmcnt(%0)" : : "n"((NB - 1) * (VSEG + KW)) : "memory");
+            const uint32_t vb0 = lds_offset(&vslot[w][b][0]) + v_lane;
+            uint32_t vw[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vw[dt] = lds_read_b32(vb0 + dt * 256);
+            f32x4_mv st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint32_t w0 = kb[b][ks >> 1][(ks & 1) * 2];
+                const uint32_t w1 = kb[b][ks >> 1][(ks & 1) * 2 + 1];
+                const u32x4 kop = {e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                   e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)};
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_mv, kop),
+                                                             __builtin_bit_cast(bf16x8_mv, qt[ks]),
+                                                             st, 0, 0, 0);
+            }
+            float x[4];
+            bool need = m_col == NEG_INF;
+            float lmax = NEG_INF;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = (ut[b] + 4 * lg + i < lim) ? st[i] * scale_log2 : NEG_INF;
+                lmax = fmaxf(lmax, x[i]);
+            }
+            need |= lmax > m_col + kRescaleThreshold;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                const float mn = fmaxf(m_col, max4_lanes(lmax));
+                const float alpha = (m_col == NEG_INF) ? 0.f : fast_exp2(m_col - mn);
+                m_col = mn;
+                acc_l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+            }
+            const float mneg = (m_col == NEG_INF) ? 0.f : -m_col;
+            const uint32_t p01 = pack_bf16x2(fast_exp2(x[0] + mneg), fast_exp2(x[1] + mneg));
+            const uint32_t p23 = pack_bf16x2(fast_exp2(x[2] + mneg), fast_exp2(x[3] + mneg));
+            const s16x4_mv pt = __builtin_bit_cast(s16x4_mv, (uint64_t)p01 | ((uint64_t)p23 << 32));
+            acc_l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones_a, pt, acc_l, 0, 0, 0);
+            lds_b32_wait<DT>(vw);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const s16x4_mv va = __builtin_bit_cast(
+                    s16x4_mv, (uint64_t)e4m3x2_to_bf16x2<false>(vw[dt]) |
+                                  ((uint64_t)e4m3x2_to_bf16x2<true>(vw[dt]) << 32));
+                acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pt, acc_o[dt], 0, 0, 0);
+            }
+        };
+
+#pragma unroll
+        for (int b = 0; b < NB; ++b) issue(b, b);
+        for (int i = 0; i < n; i += NB) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (nv[b] > 0) process(b);
+                issue(b, i + NB + b);
+            }
+        }
+    }
+
+    const float lsum = __shfl(acc_l[0], l16);
+    if (!col_ok) return;
+    const int64_t rid = ((int64_t)s * num_q_heads + (int64_t)g * G + hh) * ksplit + k;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        *(float4 *)(x_o + rid * D + dt * 16 + lg * 4) =
+            make_float4(acc_o[dt][0] * v_scale, acc_o[dt][1] * v_scale, acc_o[dt][2] * v_scale,
+                        acc_o[dt][3] * v_scale);
+    if (lg == 0) *(float2 *)(x_ml + rid * 2) = make_float2(m_col, lsum);
 }
 
 // Merge the nrec partial records (m_k: max in log2 units, l_k: sum, o_k:
@@ -1940,7 +2129,8 @@ static hipError_t launch_stream_mma(const DecodeArgs &a, hipStream_t stream, int
 }
 
 template <int D, int B, int G, bool AP>
-static void launch_stream_fp8_as(const DecodeArgs &a, hipStream_t stream) {
+static void launch_stream_fp8_as(const DecodeArgs &a, hipStream_t stream, int len_skip = 0,
+                                 int force_records = 0) {
     hipLaunchKernelGGL((decode_stream_fp8_kernel<D, B, G, kFp8Waves, AP>),
                        dim3(cdiv(a.stream_waves, kFp8Waves)), dim3(kFp8Waves * 64),
                        (size_t)(a.num_seqs + 1) * sizeof(int), stream, (bf16_t *)a.out,
@@ -1949,7 +2139,7 @@ static void launch_stream_fp8_as(const DecodeArgs &a, hipStream_t stream) {
                        a.max_blocks_per_seq, max_tokens(a), a.num_blocks, kernel_waves(a),
                        a.scale * kLog2e * a.k_scale, a.v_scale, a.ws_o, a.ws_ml, a.ws_scan,
                        (const bf16_t *)a.new_key, (const bf16_t *)a.new_value, 1.0f / a.k_scale,
-                       1.0f / a.v_scale);
+                       1.0f / a.v_scale, len_skip, force_records);
 }
 
 template <int D, int B, int G>
@@ -2101,6 +2291,16 @@ int prefix_splits(int num_seqs, int num_q_heads, int num_kv_heads, int prefix_to
 template <int D, int B, int G>
 static hipError_t launch_prefix_as(const DecodeArgs &a, const PrefixArgs &p, hipStream_t stream) {
     const int64_t waves = (int64_t)a.num_kv_heads * cdiv(a.num_seqs, 16 / G) * p.ksplit;
+    if (a.kv_fp8) {
+        hipLaunchKernelGGL((decode_prefix_fp8_kernel<D, B, G, kMmaWaves>),
+                           dim3((unsigned)cdiv_i64(waves, kMmaWaves)), dim3(kMmaWaves * 64), 0,
+                           stream, (const bf16_t *)a.query, (const uint8_t *)a.key_cache,
+                           (const uint8_t *)a.value_cache, p.prefix_table, a.context_lens,
+                           a.num_seqs, a.num_q_heads, a.num_kv_heads, a.num_blocks,
+                           p.prefix_tokens, p.ksplit, a.scale * kLog2e * a.k_scale, a.v_scale,
+                           p.x_o, p.x_ml);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((decode_prefix_mma_kernel<D, B, G, kMmaWaves>),
                        dim3((unsigned)cdiv_i64(waves, kMmaWaves)), dim3(kMmaWaves * 64), 0, stream,
                        (const bf16_t *)a.query, (const bf16_t *)a.key_cache,
@@ -2123,7 +2323,7 @@ static hipError_t prefix_by_group(const DecodeArgs &a, const PrefixArgs &p, hipS
 
 hipError_t launch_decode_prefix(const DecodeArgs &a, const PrefixArgs &p, hipStream_t stream) {
     if (a.num_seqs == 0 || p.prefix_tokens == 0) return hipSuccess;
-    if (a.dtype != 1 || a.kv_fp8) return hipErrorNotSupported;
+    if (a.dtype != 1) return hipErrorNotSupported;
     if (a.head_dim == 64)
         return a.block_size == 16 ? prefix_by_group<64, 16>(a, p, stream)
                                   : prefix_by_group<64, 32>(a, p, stream);
@@ -2131,8 +2331,23 @@ hipError_t launch_decode_prefix(const DecodeArgs &a, const PrefixArgs &p, hipStr
                               : prefix_by_group<128, 32>(a, p, stream);
 }
 
+template <int D, int B, int G>
+static hipError_t launch_suffix_fp8(const DecodeArgs &a, int len_skip, hipStream_t stream) {
+    launch_stream_fp8_as<D, B, G, false>(a, stream, len_skip, 1);
+    return hipGetLastError();
+}
+
 template <int D, int B>
 static hipError_t suffix_by_group(const DecodeArgs &a, int len_skip, hipStream_t stream) {
+    if (a.kv_fp8) {
+        switch (a.num_q_heads / a.num_kv_heads) {
+            case 1: return launch_suffix_fp8<D, B, 1>(a, len_skip, stream);
+            case 2: return launch_suffix_fp8<D, B, 2>(a, len_skip, stream);
+            case 4: return launch_suffix_fp8<D, B, 4>(a, len_skip, stream);
+            case 8: return launch_suffix_fp8<D, B, 8>(a, len_skip, stream);
+        }
+        return hipErrorNotSupported;
+    }
     switch (a.num_q_heads / a.num_kv_heads) {
         case 1: return launch_stream_mma<D, B, 1>(a, stream, len_skip, 1);
         case 2: return launch_stream_mma<D, B, 2>(a, stream, len_skip, 1);
@@ -2144,7 +2359,7 @@ static hipError_t suffix_by_group(const DecodeArgs &a, int len_skip, hipStream_t
 
 hipError_t launch_decode_suffix(const DecodeArgs &a, int len_skip, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
-    if (a.dtype != 1 || a.kv_fp8 || a.stream_waves == 0 || a.new_key) return hipErrorNotSupported;
+    if (a.dtype != 1 || a.stream_waves == 0 || a.new_key) return hipErrorNotSupported;
     if (a.head_dim == 64)
         return a.block_size == 16 ? suffix_by_group<64, 16>(a, len_skip, stream)
                                   : suffix_by_group<64, 32>(a, len_skip, stream);

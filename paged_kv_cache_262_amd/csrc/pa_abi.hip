@@ -694,14 +694,20 @@ size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_h
     return p.total() > kMinWorkspace ? p.total() : kMinWorkspace;
 }
 
-pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_cache,
-                                  const void *value_cache, const int32_t *block_tables,
-                                  const int32_t *context_lens, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t block_size, int32_t max_blocks_per_seq,
-                                  int64_t num_blocks, int32_t max_context_len,
-                                  int32_t prefix_blocks, float scale, void *workspace,
-                                  size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode_shared_prefix and pa_decode_fp8_shared_prefix: the same passes
+// over bf16 pools or over e4m3 pools (fp8, with their two scales).
+pa_status shared_prefix_decode(void *out, const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int64_t num_blocks,
+                               int32_t max_context_len, int32_t prefix_blocks, float scale,
+                               bool fp8, float k_scale, float v_scale, void *workspace,
+                               size_t workspace_bytes, void *stream) {
     pa_status s = check_common(num_q_heads, num_kv_heads, head_dim, block_size, PA_BF16);
     if (s != PA_OK) return s;
     if (num_seqs < 0 || num_seqs > pa::kStreamMaxSeqs)
@@ -736,6 +742,11 @@ pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_
                      max_blocks_per_seq, num_blocks, plan.suffix_max_len, 0, scale, PA_BF16,
                      workspace, workspace_bytes, true, false);
     if (s != PA_OK) return s;
+    if (fp8) {
+        st.a.kv_fp8 = 1;
+        st.a.k_scale = k_scale;
+        st.a.v_scale = v_scale;
+    }
     if (num_seqs == 0) return PA_OK;
     if (debug_checks() &&
         (s = debug_shared_prefix(block_tables, context_lens, num_seqs, max_blocks_per_seq,
@@ -772,6 +783,41 @@ pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_
     if (s != PA_OK) return s;
     if (w != PA_OK) return w;
     return hip_status(pa::launch_decode_reduce_prefix(st.a, px, caller), "decode_reduce");
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_shared_prefix(void *out, const void *query, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t max_context_len,
+                                  int32_t prefix_blocks, float scale, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return shared_prefix_decode(out, query, key_cache, value_cache, block_tables, context_lens,
+                                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, max_context_len, prefix_blocks,
+                                scale, false, 1.0f, 1.0f, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_fp8_shared_prefix(void *out, const void *query, const void *key_cache,
+                                      const void *value_cache, const int32_t *block_tables,
+                                      const int32_t *context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks,
+                                      int32_t max_context_len, int32_t prefix_blocks, float scale,
+                                      float k_scale, float v_scale, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f) || !isfinite(k_scale) || !isfinite(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be positive and finite");
+    return shared_prefix_decode(out, query, key_cache, value_cache, block_tables, context_lens,
+                                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, max_context_len, prefix_blocks,
+                                scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_append_partitions(void *out, const void *query, const void *new_key,
