@@ -250,6 +250,23 @@ def test_shared_prefix_rejects_on_the_host(lib):
     assert f(*args(S=0)) == 0  # nothing to do
 
 
+def test_fp8_shared_prefix_rejects_on_the_host(lib):
+    """pa_decode_fp8_shared_prefix: the shared-prefix checks, and the pools'
+    scales, before any device call."""
+    f = lib.pa_decode_fp8_shared_prefix
+    args = lambda S=4, mbs=10, maxL=100, pb=2, ws=None, D=128, G=4, ks=0.5, vs=0.25: (
+        None, None, None, None, None, None, S, 8 * G, 8, D, 16, mbs, 100, maxL, pb, 0.1, ks, vs,
+        ws, 0, None)
+    assert f(*args(ks=0.0)) == 1 and b"k_scale" in lib.pa_last_error()
+    assert f(*args(vs=float("inf"))) == 1
+    assert f(*args(ks=float("nan"))) == 1
+    assert f(*args(pb=-1)) == 1 and b"prefix_blocks" in lib.pa_last_error()
+    assert f(*args(S=8193)) == 2
+    assert f(*args(D=96)) == 2
+    assert f(*args()) == 3 and b"workspace" in lib.pa_last_error()
+    assert f(*args(S=0)) == 0  # nothing to do
+
+
 def test_shared_prefix_workspace_covers_suffix_and_prefix_records(lib):
     w = lib.pa_decode_shared_prefix_workspace_bytes
     w.restype = ctypes.c_size_t
