@@ -94,6 +94,28 @@ def test_shared_prefix_decode_graph():
     _replays_equal_eager("shared-prefix decode", q, out, step_into, 52)
 
 
+def test_fp8_shared_prefix_decode_graph():
+    """The same with e4m3 pools (pa_decode_fp8_shared_prefix)."""
+    from tests.test_fp8_gpu import fp8_pools
+    P, B = 4 * 16, 16
+    c = W.make_case("graph fp8 shared prefix", 944, "bf16", 8, 2, 128, B,
+                    [P + u for u in (0, 3, 40, 130, 250, 17, 90)], shared_prefix_tokens=P,
+                    extra_blocks=3)
+    kc8, vc8 = fp8_pools(c, 1.0 / 64, 1.0 / 32)
+    kc, vc = dev(kc8), dev(vc8)
+    q, bt, lens = dev(c.query), dev(c.block_tables), dev(c.context_lens)
+    maxL = int(c.context_lens.max())
+    out = torch.empty_like(q)
+    ws = binding.make_shared_prefix_workspace(q, kc, maxL, 4)
+    say("graph: fp8 shared-prefix decode")
+
+    def step_into(o):
+        binding.decode_fp8_shared_prefix(o, q, kc, vc, bt, lens, c.scale, maxL, 4, 1.0 / 64,
+                                         1.0 / 32, workspace=ws)
+
+    _replays_equal_eager("fp8 shared-prefix decode", q, out, step_into, 54)
+
+
 def test_prefill_chunk_graph():
     c = W.make_case("graph prefill", 943, "bf16", 8, 2, 128, 16, [5], new_positions=[4],
                     chunks=[(100, 700), (37, 37), (256, 1300)], extra_blocks=3)
