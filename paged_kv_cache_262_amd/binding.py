@@ -250,7 +250,8 @@ def decode_shared_prefix(out, query, key_cache, value_cache, block_tables, conte
     a = _decode_args(out, query, key_cache, value_cache, block_tables, context_lens,
                      max_context_len, 0, scale, workspace)
     if a[16] != PA_BF16:
-        raise PAError(PA_ERR_UNSUPPORTED, "the shared-prefix decode is bf16 only")
+        raise PAError(PA_ERR_UNSUPPORTED, "pa_decode_shared_prefix takes bf16 pools (FP8 pools: "
+                                          "decode_fp8_shared_prefix)")
     _check(load().pa_decode_shared_prefix(*a[:14], int(prefix_blocks), a[15], a[17], a[18],
                                           _stream(stream)))
     return out
